@@ -1,0 +1,50 @@
+"""The five workloads the measurements and parity checks run on.
+
+Shapes follow the pages' workloads (long causal sequences, head dim 128, 16-32
+heads, 8-way sequence sharding); the values are synthetic (see ``synth``).
+Assignment names: ``contiguous`` (rank r holds one run of L/N tokens),
+``striped`` (token t on rank t mod N), ``zigzag`` (2N chunks, rank r holds
+chunks r and 2N-1-r), ``ulysses`` (sequence-sharded input permuted to
+head-sharded, then one full-sequence causal attention).
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    number: int            # seeds are 1000*number + {0,1,2}
+    batch: int
+    heads: int
+    head_dim: int
+    global_len: int
+    world: int             # ring size N (or Ulysses degree P)
+    rank: int              # the rank whose share is computed (-1: every rank)
+    assign: str            # contiguous | striped | zigzag | ulysses
+    causal: bool
+    dtype: str             # "bf16" or "f32" (input and accumulation-state precision)
+    qk_std: float = 1.0
+    sampled_rows: int = 0  # 0: full oracle; else 512-row sampled check
+
+    @property
+    def share_len(self) -> int:
+        return self.global_len // self.world
+
+
+CONFIGS = {
+    "tiny_exact": Workload("tiny_exact", 1, 1, 1, 64, 256, 4, -1, "contiguous", False, "f32"),
+    "contig_rank7": Workload("contig_rank7", 2, 1, 32, 128, 8192, 8, 7, "contiguous", True, "bf16"),
+    "striped_rank0": Workload("striped_rank0", 3, 1, 32, 128, 32768, 8, 0, "striped", True, "bf16"),
+    "striped_rank0_std4": Workload("striped_rank0_std4", 3, 1, 32, 128, 32768, 8, 0, "striped", True,
+                                   "bf16", qk_std=4.0),
+    "ulysses_local": Workload("ulysses_local", 4, 1, 32, 128, 65536, 8, 0, "ulysses", True, "bf16",
+                              sampled_rows=512),
+    "zigzag_rank3": Workload("zigzag_rank3", 5, 1, 16, 128, 262144, 8, 3, "zigzag", True, "bf16",
+                             sampled_rows=512),
+}
+
+
+def get(name: str) -> Workload:
+    return CONFIGS[name]
