@@ -1,0 +1,309 @@
+#!/usr/bin/env python3
+"""Throughput of the per-device Ring Attention inner loop on one MI355X.
+
+A step is one ``ra_ring_share`` call: every ring step of one rank's share (token positions,
+tile classification, QK^T, causal mask, online softmax, PV, epilogue) on the long zigzag
+workload -- B=1, H=16, D=128, L=262144 over N=8 ranks in 16 chunks of 16384, rank 3's
+32768 queries against all 8 KV shares, bf16 inputs, fp32 accumulation. The value is
+causal-adjusted TFLOP/s: 4*D FLOPs per visible (query, key) pair per head, the pairs counted
+by the library's planner from the same position rule the kernel uses.
+
+Also reported in the same JSON line (``secondary``): the other bf16 workloads (contiguous
+rank 7 of L=8192, striped rank 0 of L=32768 at std 1 and 4, the Ulysses local step of
+L=65536 with its permutes), the LSE-merge bandwidth, the roofline of the attention kernel and
+the oracle timed on the host cores (``cpu_baseline``).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-secondary] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "causal-adjusted attention TFLOP/s per GPU share; % of bf16 MFMA peak"
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 FLOP/clk/CU
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+HEADLINE = "zigzag_rank3"
+KERNEL_SRC = os.path.join(ROOT, "ring_sequence_parallelism_ra_amd", "csrc", "attn_bf16.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_bf16_zigzag_rank3_traffic.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def to_dev(bits):
+    import numpy as np
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def ring_inputs(w):
+    """Q share and the N K/V shares of a ring workload, gathered on the device by the
+    library's own position rule."""
+    import torch
+
+    import ring_sequence_parallelism_ra_amd as ra
+    import synth
+    gq, gk, gv = synth.global_qkv(w)
+    n, L = w.world, w.global_len
+    pos = [ra.debug_positions(ra.Shard(w.assign, n, s, L)) for s in range(n)]
+    out = {}
+    for name, g in (("q", gq), ("k", gk), ("v", gv)):
+        t = to_dev(g)
+        if name == "q":
+            out["q"] = torch.index_select(t, 1, pos[w.rank]).contiguous()
+        else:
+            out[name] = [torch.index_select(t, 1, p).contiguous() for p in pos]
+        del t
+    torch.cuda.synchronize()
+    return out, (gq, gk, gv)
+
+
+def ring_pairs(w) -> int:
+    import ring_sequence_parallelism_ra_amd as ra
+    n, L, s = w.world, w.global_len, w.share_len
+    q_sh = ra.Shard(w.assign, n, w.rank, L)
+    return sum(ra.share_work(q_sh, ra.Shard(w.assign, n, src, L), s, s, True)[0] for src in range(n))
+
+
+def time_calls(fn, steps, warmup):
+    """(wall ms per call over ``steps`` back-to-back calls, mean event ms per call)."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        starts[i].record()
+        fn()
+        ends[i].record()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    ev = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    return wall, sum(ev) / len(ev), sorted(ev)[len(ev) // 2]
+
+
+def bench_ring(name, steps, warmup):
+    import torch
+
+    import ring_sequence_parallelism_ra_amd as ra
+    import synth
+    w = synth.get(name)
+    t0 = time.perf_counter()
+    inp, host = ring_inputs(w)
+    log(f"[bench] {name}: inputs ready in {time.perf_counter() - t0:.1f}s")
+    call, o, lse = ra.prepare_ring_share(inp["q"], inp["k"], inp["v"], w.rank, assign=w.assign, causal=True)
+    flops = 4 * w.head_dim * w.batch * w.heads * ring_pairs(w)
+    wall, ev_mean, ev_med = time_calls(call, steps, warmup)
+    res = {"tflops": flops / (wall * 1e-3) / 1e12, "kernel_ms_mean": ev_mean, "kernel_ms_median": ev_med,
+           "ms_per_step": wall, "flops": flops}
+    del inp, o, lse
+    torch.cuda.empty_cache()
+    return res, host, w
+
+
+def bench_ulysses(steps, warmup):
+    import torch
+
+    import ring_sequence_parallelism_ra_amd as ra
+    import synth
+    w = synth.get("ulysses_local")
+    gq, gk, gv = synth.global_qkv(w)
+    P, L, H, D, B = w.world, w.global_len, w.heads, w.head_dim, w.batch
+    s_loc = L // P
+    stacks = [to_dev(g).view(B, P, s_loc, H, D).transpose(0, 1).contiguous() for g in (gq, gk, gv)]
+    del gq, gk, gv
+    # permute bandwidth: rotate the destination rank and the tensor so that successive calls
+    # read different 64 MiB regions (24 distinct sources, 4 output buffers)
+    outs = [torch.empty((B, L, H // P, D), dtype=torch.bfloat16, device="cuda") for _ in range(4)]
+    plan = [(stacks[t], dst) for dst in range(P) for t in range(3)]
+    idx = [0]
+
+    def perm():
+        x, dst = plan[idx[0] % len(plan)]
+        ra.seq2head_permute(x, dst, out=outs[idx[0] % 4])
+        idx[0] += 1
+
+    nperm = max(steps, 24)
+    wall, ev_mean, _ = time_calls(perm, nperm, 3)
+    moved = 2 * B * L * (H // P) * D * 2  # read + write bytes per call
+    perm_gbs = moved / (ev_mean * 1e-3) / 1e9
+    # the local step itself: permute Q, K, V for rank 0, causal attention, inverse of O
+    q, k, v = (ra.seq2head_permute(x, w.rank) for x in stacks)
+    full = ra.Shard("contiguous", 1, 0, L)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H // P, L), dtype=torch.float32, device="cuda")
+
+    def attn():
+        ra.block_attn_fwd(q, k, v, causal=True, q_shard=full, kv_shard=full, o=o, lse=lse)
+
+    pairs = ra.share_work(full, full, L, L, True)[0]
+    flops = 4 * D * B * (H // P) * pairs
+    wall_a, ev_a, _ = time_calls(attn, steps, warmup)
+    o_seq = torch.empty((P, B, s_loc, H, D), dtype=torch.bfloat16, device="cuda")
+    wall_i, ev_i, _ = time_calls(lambda: ra.head2seq_permute(o, w.rank, o_seq), steps, warmup)
+    del stacks, outs, q, k, v, o, lse, o_seq
+    torch.cuda.empty_cache()
+    return {"attention_tflops": flops / (ev_a * 1e-3) / 1e12, "attention_ms": ev_a,
+            "permute_gbs": perm_gbs, "permute_pct_hbm": 100 * perm_gbs / PEAK_HBM_GBS,
+            "inverse_permute_gbs": moved / (ev_i * 1e-3) / 1e9,
+            "step_ms": 3 * moved / (perm_gbs * 1e9) * 1e3 + ev_a + ev_i}
+
+
+def bench_merge(steps, warmup):
+    import torch
+
+    import ring_sequence_parallelism_ra_amd as ra
+    B, S, H, D = 1, 32768, 16, 128  # one share of the long zigzag workload, fp32 state
+    sets = []
+    for i in range(3):
+        g = torch.Generator(device="cuda").manual_seed(i)
+        sets.append((torch.randn((B, S, H, D), device="cuda", generator=g),
+                     torch.randn((B, H, S), device="cuda", generator=g),
+                     torch.randn((B, S, H, D), device="cuda", generator=g),
+                     torch.randn((B, H, S), device="cuda", generator=g)))
+    idx = [0]
+
+    def merge():
+        a = sets[idx[0] % 3]
+        ra.lse_merge(*a)
+        idx[0] += 1
+
+    _, ev, _ = time_calls(merge, max(steps, 12), warmup)
+    moved = B * S * H * (3 * 4 * D + 3 * 4)
+    del sets
+    torch.cuda.empty_cache()
+    return {"gbs": moved / (ev * 1e-3) / 1e9, "pct_hbm": 100 * moved / (ev * 1e-3) / 1e9 / PEAK_HBM_GBS,
+            "ms": ev, "shape": [B, S, H, D]}
+
+
+def cpu_baseline(host, w, budget_s):
+    """The fp64 oracle timed on this host: batches of sampled query rows (all heads) of the
+    headline share, each against every key up to its position, until ``budget_s`` is used."""
+    import numpy as np
+
+    import synth
+    from oracle import attention as OA
+    from oracle import positions as OP
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        cores = max(i["num_threads"] for i in blas) if blas else 1
+    except Exception:
+        cores = os.cpu_count() or 1
+    gq, gk, gv = host
+    n, r, L = w.world, w.rank, w.global_len
+    pos = OP.positions(w.assign, n, r, L)
+    rows = synth.sample_rows(1000 * w.number, w.share_len, chunk_len=L // (2 * n))
+    rows = np.random.default_rng(0).permutation(rows)
+    batch = 16
+    done_rows, pairs, t0 = 0, 0, time.perf_counter()
+    for i in range(0, len(rows), batch):
+        rb = np.sort(rows[i:i + batch])
+        qpos = pos[rb]
+        kmax = int(qpos.max()) + 1
+        q = synth.bf16_bits_to_f32(np.ascontiguousarray(gq[:, qpos]))
+        k = synth.bf16_bits_to_f32(gk[:, :kmax])
+        v = synth.bf16_bits_to_f32(gv[:, :kmax])
+        OA.attention(q, k, v, qpos, np.arange(kmax), True)
+        done_rows += len(rb)
+        pairs += int((qpos + 1).sum()) * w.heads * w.batch
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    flops = 4 * w.head_dim * pairs
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{done_rows} sampled query rows x {w.heads} heads of {w.name} ({pairs} visible pairs, "
+                      f"fp64 numpy, {dt:.1f}s incl. bf16->fp64 conversion)"}
+
+
+def traffic_for(kernel_ms_launch):
+    """HBM bytes per launch from committed rocprofv3 --pmc counters, if they were taken on the
+    current kernel source; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_sha256_16") != kernel_hash():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU's share only: this build runs on a single MI355X and has no "
+              "multi-GPU path (each rank would run the same ra_ring_share on its own share). "
+              "Run with --gpus 1.", file=sys.stderr, flush=True)
+        sys.exit(2)
+
+    import torch
+    import ring_sequence_parallelism_ra_amd as ra  # noqa: F401  (fails loudly if libra.so is missing)
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+
+    head, host, w = bench_ring(HEADLINE, args.steps, args.warmup)
+    log(f"[bench] {HEADLINE}: {head['tflops']:.1f} TFLOP/s, kernel {head['kernel_ms_mean']:.3f} ms")
+    achieved = head["flops"] / (head["kernel_ms_mean"] * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic_for(head["kernel_ms_mean"]),
+                "kernel": "attn_bf16_kernel<128, OutBf16>", "kernel_ms": round(head["kernel_ms_mean"], 4),
+                "flops_per_launch": head["flops"]}
+
+    secondary = {}
+    if not args.no_secondary:
+        for name in ("contig_rank7", "striped_rank0", "striped_rank0_std4"):
+            r, _, _ = bench_ring(name, args.steps, args.warmup)
+            secondary[name] = {"tflops": round(r["tflops"], 2), "pct_bf16_peak": round(100 * r["tflops"] / PEAK_BF16_TFLOPS, 2),
+                               "kernel_ms": round(r["kernel_ms_mean"], 4)}
+            log(f"[bench] {name}: {r['tflops']:.1f} TFLOP/s")
+        u = bench_ulysses(args.steps, args.warmup)
+        secondary["ulysses_local"] = {k: round(v, 3) for k, v in u.items()}
+        log(f"[bench] ulysses_local: attention {u['attention_tflops']:.1f} TFLOP/s, permute {u['permute_gbs']:.0f} GB/s")
+        m = bench_merge(args.steps, args.warmup)
+        secondary["lse_merge"] = {k: (round(v, 3) if isinstance(v, float) else v) for k, v in m.items()}
+        log(f"[bench] lse_merge: {m['gbs']:.0f} GB/s")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(host, w, args.cpu_seconds)
+        log(f"[bench] cpu_baseline: {cpu['value']:.4f} TFLOP/s on {cpu['cores']} threads")
+
+    line = {"metric": METRIC, "value": round(head["tflops"], 2), "unit": "TFLOP/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(head["ms_per_step"], 4),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+            "data": "synthetic",
+            "config": {"workload": HEADLINE, "batch": w.batch, "heads": w.heads, "head_dim": w.head_dim,
+                       "global_len": w.global_len, "world": w.world, "rank": w.rank, "assign": w.assign,
+                       "share_len": w.share_len, "causal": True,
+                       "pct_bf16_peak": round(100 * head["tflops"] / PEAK_BF16_TFLOPS, 2)},
+            "roofline": roofline, "cpu_baseline": cpu, "secondary": secondary}
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

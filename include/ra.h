@@ -1,0 +1,185 @@
+/*
+ * ra.h -- C ABI of the per-device Ring Attention inner loop for MI355X (gfx950).
+ *
+ * Pages this interface follows (cited by title and section):
+ *   [Digest] "从 Ring Attention 到 DeepSpeed Ulysses，再到 USP 统一框架" (jsqmd.com digest)
+ *   [Notes]  "主流序列并行(SP)方案对比 + 大模型通信原语" (hzhuang.org notes)
+ *   [Q14]    "序列并行（Sequence Parallelism）解决了什么问题？和 TP 是什么关系？" (playoffer)
+ *
+ * Conventions shared by every call
+ *   - Tensor pointers are DEVICE pointers owned by the caller. The library never
+ *     allocates, frees or keeps caller memory. The one exception is the ring call's
+ *     k_shares / v_shares: HOST arrays holding N device pointers.
+ *   - Q, K, V, O are [B, S, H, D] row-major with D contiguous (the [bs, seq, heads,
+ *     head_dim] layout of the pages' ring example, [Digest] §10). LSE is fp32
+ *     [B, H, S], natural log.
+ *   - Every call enqueues work on the caller's stream and returns at once; nothing
+ *     synchronises the device. A fault inside a kernel surfaces at the caller's next
+ *     synchronisation.
+ *   - Arguments are validated on the host before anything is launched, so every
+ *     error code below is produced without touching the GPU. Calls return RA_OK or a
+ *     negative status; ra_last_error() then describes the failure (a thread-local
+ *     string owned by the library, valid until the next call on the same thread).
+ *   - Nothing throws across the ABI. Calls on different streams may run concurrently
+ *     as long as they do not write the same memory.
+ *   - Device pointers must be 16-byte aligned (128-bit loads and stores).
+ *   - Empty inputs (B, H or a sequence length of 0) are valid and launch nothing.
+ */
+#ifndef RA_H_
+#define RA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define RA_OK 0
+#define RA_ERR_INVALID_ARG (-1)  /* null pointer, rank >= N, N < 1, negative size, bad step range */
+#define RA_ERR_UNSUPPORTED (-2)  /* dtype not in {RA_F32, RA_BF16}, D not in {64, 128}, N > RA_MAX_WORLD */
+#define RA_ERR_SHAPE (-3)        /* H % P != 0, L % N != 0, L % 2N != 0 (zigzag), sizes disagree */
+#define RA_ERR_MISALIGNED (-4)   /* a device pointer is not 16-byte aligned */
+#define RA_ERR_HIP (-5)          /* a HIP launch error */
+
+#define RA_MAX_WORLD 64          /* largest ring size N accepted by ra_ring_share */
+
+typedef enum { RA_F32 = 0, RA_BF16 = 1 } ra_dtype;
+
+/* Token -> rank assignment of a sequence of global_len tokens over world ranks.
+ *   RA_CONTIGUOUS: rank r holds tokens [r*L/N, (r+1)*L/N)        ([Digest] §3.4, §4 listing)
+ *   RA_STRIPED:    token t lives on rank t mod N                  ([Digest] §4)
+ *   RA_ZIGZAG:     2N equal chunks; rank r holds chunks r, 2N-1-r ([Digest] §6 item 1)
+ * Local row i of a share is the i-th smallest global position the rank holds. */
+typedef enum { RA_CONTIGUOUS = 0, RA_STRIPED = 1, RA_ZIGZAG = 2 } ra_assign;
+
+typedef struct {
+  int32_t assign;      /* ra_assign */
+  int32_t world;       /* N >= 1 */
+  int32_t rank;        /* 0 <= rank < N */
+  int64_t global_len;  /* L; L % N == 0 (L % 2N == 0 for zigzag) */
+} ra_shard;
+
+/*
+ * ra_block_attn_fwd -- one ring step's block attention: local Q against one KV block
+ * ("flash_attn_block(Q_local, K, V) -> (out, lse)" in the ring loop of [Digest] §3.3;
+ * the definition softmax(Q K^T / sqrt(d)) V is [Digest] §2).
+ *
+ *   q     [B, Sq, H, D]  in_dtype           k, v  [B, Sk, H, D]  in_dtype
+ *   o     [B, Sq, H, D]  o_dtype (output)   lse   [B, H, Sq]     fp32 (output)
+ *   causal: if non-zero, key j is visible to query i iff pos_kv(j) <= pos_q(i), the
+ *     positions coming from q_sh / kv_sh (the mask is taken by global position,
+ *     [Q14] engineering notes; diagonal included, [Digest] §3.4). Then Sq must equal
+ *     q_sh->global_len / q_sh->world and Sk likewise for kv_sh. If zero, every key is
+ *     visible and q_sh / kv_sh may be NULL.
+ *   scale: logit scale; <= 0 selects 1/sqrt(D) (softmax_scale=None, [Digest] §10).
+ * Output: O normalised, LSE = ln(sum over visible keys of exp(scale * q.k)). A row with
+ * no visible key gets O = 0 and LSE = -inf.
+ * in_dtype RA_BF16 runs bf16 MFMA with fp32 accumulation; RA_F32 runs fp32 FMA.
+ * D must be 64 or 128. Sq and Sk may be any non-negative size (ragged tails are masked).
+ */
+int ra_block_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                      int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t D,
+                      int in_dtype, int o_dtype, int causal,
+                      const ra_shard* q_sh, const ra_shard* kv_sh, float scale,
+                      hipStream_t stream);
+
+/*
+ * ra_lse_merge -- merge a block result into an accumulated one, in place
+ * ("online_softmax_merge" of [Digest] §3.3, "merge_lse" and its formula in [Digest] §6
+ * item 3):
+ *     lse = max(a, b) + log(1 + exp(-|a - b|));  O = O_acc e^(a - lse) + O_blk e^(b - lse)
+ * with a = lse_acc, b = lse_blk, O's normalised. A side whose lse is -inf contributes
+ * nothing; two empty sides give O = 0, lse = -inf.
+ *   o_acc [B, S, H, D] acc_dtype (in/out)   lse_acc [B, H, S] fp32 (in/out)
+ *   o_blk [B, S, H, D] blk_dtype            lse_blk [B, H, S] fp32
+ * D may be any positive multiple of 8. Merges in any order give the same result up to
+ * rounding ([Digest] §3.2).
+ */
+int ra_lse_merge(void* o_acc, float* lse_acc, const void* o_blk, const float* lse_blk,
+                 int64_t B, int64_t H, int64_t S, int64_t D, int acc_dtype, int blk_dtype,
+                 hipStream_t stream);
+
+/* Bytes of workspace ra_ring_share needs to keep the running state between calls:
+ * fp32 O [B, S, H, D] plus fp32 running max and running sum [B, H, S] each. */
+size_t ra_ring_share_workspace_bytes(int64_t B, int64_t H, int64_t S_loc, int64_t D);
+
+/*
+ * ra_ring_share -- every ring step of one rank's share on one stream ([Digest] §3.1 and
+ * the loop of §3.3): step s attends the local Q to the KV share of rank
+ * src = (rank - s) mod N (round 0 is local; KV moves to rank+1), folding each block into
+ * the running (m, l, O) by the online-softmax update of [Digest] §3.2.
+ *   q                    [B, S_loc, H, D] in_dtype, rank's share
+ *   k_shares, v_shares   HOST arrays of N device pointers; entry i is rank i's share
+ *                        [B, S_loc, H, D] in_dtype
+ *   o, lse               outputs as in ra_block_attn_fwd, written when the last step
+ *                        (start_step + num_steps == N) has run
+ *   assign, causal       token assignment of the global sequence (L = N * S_loc) and
+ *                        whether the causal mask by global position applies
+ *   start_step, num_steps  run steps [start_step, start_step + num_steps), in ring order
+ *   ws, ws_bytes         running state (size from ra_ring_share_workspace_bytes). May be
+ *                        NULL when start_step == 0 and num_steps == N (the state then stays
+ *                        in registers). A call that ends before step N stores the state in
+ *                        ws; a call with start_step > 0 resumes from it. The state is
+ *                        opaque, valid only for the same q, in_dtype, scale and shape.
+ * The result does not depend on how the N steps are split across calls, up to rounding.
+ */
+int ra_ring_share(const void* q, const void* const* k_shares, const void* const* v_shares,
+                  void* o, float* lse, int64_t B, int64_t H, int64_t S_loc, int64_t D,
+                  int N, int rank, int assign, int causal, int in_dtype, int o_dtype,
+                  float scale, int start_step, int num_steps, void* ws, size_t ws_bytes,
+                  hipStream_t stream);
+
+/*
+ * ra_seq2head_permute -- the local data movement of the Ulysses all-to-all ([Digest] §5.1,
+ * [Notes] §3): sequence-sharded [bs, L/P, H, d] on each of P ranks to head-sharded
+ * [bs, L, H/P, d], rank p taking heads [p*H/P, (p+1)*H/P), its full sequence ordered by
+ * source rank.
+ *   forward (inverse == 0): in  = [P, B, S_loc, H, D] (the P ranks' shares, stacked)
+ *       dst_rank >= 0: out = [B, P*S_loc, H/P, D],
+ *                      out[b, src*S_loc + s, h', :] = in[src, b, s, dst_rank*H/P + h', :]
+ *       dst_rank == -1: out = [P, B, P*S_loc, H/P, D], every rank's result stacked
+ *   inverse (inverse != 0): in = the forward output for dst_rank (or the stack for -1),
+ *       out = [P, B, S_loc, H, D]; writes only the head slice(s) of dst_rank (all for -1)
+ *       and leaves the other heads of out untouched.
+ * dtype gives the element size (RA_BF16: 2 bytes, RA_F32: 4); the copy is bit-exact.
+ * H % P != 0 is RA_ERR_SHAPE (the head-count constraint of [Digest] §5.3).
+ */
+int ra_seq2head_permute(const void* in, void* out, int64_t B, int64_t P, int64_t S_loc,
+                        int64_t H, int64_t D, int dtype, int dst_rank, int inverse,
+                        hipStream_t stream);
+
+/* Thread-local description of the last failure on this thread ("" after success). */
+const char* ra_last_error(void);
+
+/*
+ * Planner and debug hooks.
+ *
+ * ra_share_work (host only, no GPU): causal work of one Q share against one KV share,
+ * from the same position functions the kernels use. out[0] = visible (query, key) pairs,
+ * out[1..3] = full / partial / skip tiles of block_m x block_n over [Sq, Sk] (a tile is
+ * full when every existing pair in it is visible, skip when none is). Attention FLOPs are
+ * 4 * D * out[0] per (batch, head). Returns a status like the calls above.
+ */
+int ra_share_work(const ra_shard* q_sh, const ra_shard* kv_sh, int64_t Sq, int64_t Sk,
+                  int causal, int64_t block_m, int64_t block_n, int64_t out[4]);
+
+/* Tile shape (rows of Q, keys of K/V) the attention kernel uses for in_dtype and D. */
+int ra_tile_shape(int in_dtype, int64_t D, int64_t* block_m, int64_t* block_n);
+
+/* Device: out[i] = global position of local row i of sh's share (i < L/N), int64. */
+int ra_debug_positions(const ra_shard* sh, int64_t* out, hipStream_t stream);
+
+/* Device: out[i*Sk + j] = 1 if key j of kv_sh's share is visible to query i of q_sh's
+ * share under the causal mask, else 0; evaluated by the kernels' own mask function. */
+int ra_debug_mask(const ra_shard* q_sh, const ra_shard* kv_sh, int64_t Sq, int64_t Sk,
+                  uint8_t* out, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RA_H_ */

@@ -1,0 +1,183 @@
+"""torch-facing wrappers of the C ABI (same names as ``include/ra.h`` without the ``ra_`` prefix).
+
+PyTorch supplies device memory and streams only; the wrappers check tensor shapes/dtypes,
+allocate outputs when none are given, and pass raw pointers to the HIP library.
+"""
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from ._lib import ASSIGN, BF16, F32, Shard, check, lib
+
+_DT = {torch.float32: F32, torch.bfloat16: BF16}
+_TORCH_DT = {F32: torch.float32, BF16: torch.bfloat16}
+
+
+def _dt(t: torch.Tensor) -> int:
+    try:
+        return _DT[t.dtype]
+    except KeyError:
+        raise TypeError(f"unsupported dtype {t.dtype}; use float32 or bfloat16") from None
+
+
+def _stream(stream):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _p(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None and t.numel() else None
+
+
+def _need(t, name):
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor")
+
+
+def _shard(sh):
+    if sh is None:
+        return None
+    if not isinstance(sh, Shard):
+        sh = Shard(*sh)
+    return ctypes.byref(sh)
+
+
+def block_attn_fwd(q, k, v, *, causal=False, q_shard=None, kv_shard=None, scale=0.0, out_dtype=None,
+                   o=None, lse=None, stream=None):
+    """O, LSE of q [B,Sq,H,D] against one KV block k, v [B,Sk,H,D]; see ra_block_attn_fwd."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n)
+    b, sq, h, d = q.shape
+    sk = k.shape[1]
+    if k.shape != (b, sk, h, d) or v.shape != k.shape or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("k/v must be [B, Sk, H, D] with q's B, H, D and dtype")
+    od = out_dtype or q.dtype
+    if o is None:
+        o = torch.empty((b, sq, h, d), dtype=od, device=q.device)
+    if lse is None:
+        lse = torch.empty((b, h, sq), dtype=torch.float32, device=q.device)
+    check(lib.ra_block_attn_fwd(_p(q), _p(k), _p(v), _p(o), _p(lse), b, h, sq, sk, d, _dt(q), _dt(o),
+                                1 if causal else 0, _shard(q_shard), _shard(kv_shard), float(scale),
+                                _stream(stream)))
+    return o, lse
+
+
+def ring_share_workspace_bytes(B, H, S_loc, D) -> int:
+    return int(lib.ra_ring_share_workspace_bytes(B, H, S_loc, D))
+
+
+def ring_share_workspace(B, H, S_loc, D, device="cuda"):
+    return torch.empty(ring_share_workspace_bytes(B, H, S_loc, D), dtype=torch.uint8, device=device)
+
+
+def prepare_ring_share(q, k_shares, v_shares, rank, *, assign="contiguous", causal=True, scale=0.0,
+                       out_dtype=None, start_step=0, num_steps=None, ws=None, o=None, lse=None,
+                       stream=None):
+    """Marshal the arguments of ra_ring_share once; returns (call, o, lse) where ``call()``
+    enqueues the whole ring loop on the stream (for repeated launches)."""
+    _need(q, "q")
+    b, s, h, d = q.shape
+    n = len(k_shares)
+    if len(v_shares) != n:
+        raise ValueError("k_shares and v_shares differ in length")
+    for t in list(k_shares) + list(v_shares):
+        _need(t, "share")
+        if t.shape != q.shape or t.dtype != q.dtype:
+            raise ValueError("every K/V share must match q's shape and dtype")
+    num = n - start_step if num_steps is None else num_steps
+    od = out_dtype or q.dtype
+    if o is None:
+        o = torch.empty((b, s, h, d), dtype=od, device=q.device)
+    if lse is None:
+        lse = torch.empty((b, h, s), dtype=torch.float32, device=q.device)
+    kp = (ctypes.c_void_p * n)(*[t.data_ptr() for t in k_shares])
+    vp = (ctypes.c_void_p * n)(*[t.data_ptr() for t in v_shares])
+    ws_p, ws_n = (_p(ws), ws.numel()) if ws is not None else (None, 0)
+    args = (_p(q), kp, vp, _p(o), _p(lse), b, h, s, d, n, rank, ASSIGN.get(assign, assign),
+            1 if causal else 0, _dt(q), _dt(o), float(scale), start_step, num, ws_p, ws_n,
+            _stream(stream))
+    keep = (k_shares, v_shares, ws)
+
+    def call():
+        _ = keep
+        check(lib.ra_ring_share(*args))
+
+    return call, o, lse
+
+
+def ring_share(q, k_shares, v_shares, rank, **kw):
+    """Every ring step of ``rank``'s share; see ra_ring_share. Returns (O, LSE)."""
+    call, o, lse = prepare_ring_share(q, k_shares, v_shares, rank, **kw)
+    call()
+    return o, lse
+
+
+def lse_merge(o_acc, lse_acc, o_blk, lse_blk, stream=None):
+    """In-place merge of (o_blk, lse_blk) into (o_acc, lse_acc); see ra_lse_merge."""
+    for t, nme in ((o_acc, "o_acc"), (lse_acc, "lse_acc"), (o_blk, "o_blk"), (lse_blk, "lse_blk")):
+        _need(t, nme)
+    b, s, h, d = o_acc.shape
+    if o_blk.shape != o_acc.shape or lse_acc.shape != (b, h, s) or lse_blk.shape != (b, h, s):
+        raise ValueError("shape mismatch")
+    if lse_acc.dtype != torch.float32 or lse_blk.dtype != torch.float32:
+        raise ValueError("lse tensors must be float32")
+    check(lib.ra_lse_merge(_p(o_acc), _p(lse_acc), _p(o_blk), _p(lse_blk), b, h, s, d, _dt(o_acc),
+                           _dt(o_blk), _stream(stream)))
+    return o_acc, lse_acc
+
+
+def seq2head_permute(x, dst_rank, out=None, stream=None):
+    """x [P, B, S_loc, H, D] -> [B, P*S_loc, H/P, D] for dst_rank (or the stack of all ranks
+    [P, B, P*S_loc, H/P, D] for dst_rank=-1); see ra_seq2head_permute."""
+    _need(x, "x")
+    p, b, s, h, d = x.shape
+    shape = (b, p * s, h // p, d) if dst_rank >= 0 else (p, b, p * s, h // p, d)
+    if out is None:
+        out = torch.empty(shape, dtype=x.dtype, device=x.device)
+    check(lib.ra_seq2head_permute(_p(x), _p(out), b, p, s, h, d, _dt(x), dst_rank, 0, _stream(stream)))
+    return out
+
+
+def head2seq_permute(y, dst_rank, out, stream=None):
+    """Inverse: write y (dst_rank's head-sharded tensor, or the stack) back into
+    out [P, B, S_loc, H, D], touching only dst_rank's heads (all for -1)."""
+    _need(y, "y")
+    _need(out, "out")
+    p, b, s, h, d = out.shape
+    check(lib.ra_seq2head_permute(_p(y), _p(out), b, p, s, h, d, _dt(out), dst_rank, 1, _stream(stream)))
+    return out
+
+
+def share_work(q_shard, kv_shard, Sq, Sk, causal=True, block_m=128, block_n=64):
+    """(visible pairs, full tiles, partial tiles, skip tiles); host only, no GPU."""
+    out = (ctypes.c_int64 * 4)()
+    check(lib.ra_share_work(_shard(q_shard), _shard(kv_shard), Sq, Sk, 1 if causal else 0, block_m,
+                            block_n, out))
+    return tuple(out)
+
+
+def tile_shape(in_dtype=BF16, D=128):
+    bm, bn = ctypes.c_int64(), ctypes.c_int64()
+    check(lib.ra_tile_shape(in_dtype, D, ctypes.byref(bm), ctypes.byref(bn)))
+    return bm.value, bn.value
+
+
+def debug_positions(shard, device="cuda", stream=None):
+    sh = shard if isinstance(shard, Shard) else Shard(*shard)
+    out = torch.empty(sh.global_len // sh.world, dtype=torch.int64, device=device)
+    check(lib.ra_debug_positions(ctypes.byref(sh), _p(out), _stream(stream)))
+    return out
+
+
+def debug_mask(q_shard, kv_shard, Sq, Sk, device="cuda", stream=None):
+    out = torch.empty((Sq, Sk), dtype=torch.uint8, device=device)
+    check(lib.ra_debug_mask(_shard(q_shard), _shard(kv_shard), Sq, Sk, _p(out), _stream(stream)))
+    return out
+
+
+def torch_dtype(code: int):
+    return _TORCH_DT[code]

@@ -1,0 +1,69 @@
+"""Build the HIP library ``libra.so`` in-tree for gfx950.
+
+Every HIP source is compiled with ``hipcc --offload-arch=gfx950 -O3`` and with packed
+fp32 VALU instructions disabled (``-Xclang -target-feature -Xclang -packed-fp32-ops``).
+Objects go to ``_build/`` next to this file; the shared library lands next to this file.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+BUILD = os.path.join(HERE, "_build")
+LIB = os.path.join(HERE, "libra.so")
+SOURCES = ["ra_api.cpp", "attn_bf16.hip", "attn_f32.hip", "movement.hip"]
+ARCH = "gfx950"
+
+
+def hipcc() -> str:
+    for cand in (shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found")
+
+
+def flags() -> list:
+    return [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            "-Wno-unused-command-line-argument", "-I", os.path.join(HERE, "..", "include")]
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    cc = hipcc()
+    procs = []
+    objs = []
+    for src in SOURCES:
+        obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+        objs.append(obj)
+        cmd = [cc, *flags(), "-c", os.path.join(CSRC, src), "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))
+    errors = []
+    for src, p in procs:
+        out, _ = p.communicate()
+        text = out.decode(errors="replace")
+        # hipcc's host pass does not know the packed-fp32 feature; that warning is expected.
+        lines = [ln for ln in text.splitlines() if "packed-fp32-ops" not in ln]
+        if p.returncode != 0:
+            errors.append(f"{src}:\n" + "\n".join(lines))
+        elif verbose and lines:
+            print("\n".join(lines))
+    if errors:
+        raise RuntimeError("HIP build failed:\n" + "\n".join(errors))
+    tmp = LIB + ".tmp"
+    cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)
+    if r.returncode != 0:
+        raise RuntimeError("link failed:\n" + r.stdout.decode(errors="replace"))
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

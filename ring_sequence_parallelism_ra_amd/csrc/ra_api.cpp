@@ -1,0 +1,311 @@
+// Host side of the C ABI declared in include/ra.h: argument validation (all of it before any
+// launch, so every error path runs without a GPU), the ring step order, workspace layout,
+// the planner counts and the kernel launches.
+//
+// [Digest] = "从 Ring Attention 到 DeepSpeed Ulysses，再到 USP 统一框架" (jsqmd.com).
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "ra_internal.h"
+
+namespace {
+
+thread_local char g_err[512];
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_err[0] = 0;
+  return RA_OK;
+}
+
+bool misaligned(const void* p) { return ((uintptr_t)p & 15u) != 0; }
+
+bool dtype_ok(int d) { return d == RA_F32 || d == RA_BF16; }
+
+int check_shard(const ra_shard* sh, int64_t S, const char* what) {
+  if (!sh) return fail(RA_ERR_INVALID_ARG, "%s: shard descriptor is NULL", what);
+  if (sh->assign < RA_CONTIGUOUS || sh->assign > RA_ZIGZAG)
+    return fail(RA_ERR_INVALID_ARG, "%s: unknown assignment %d", what, sh->assign);
+  if (sh->world < 1) return fail(RA_ERR_INVALID_ARG, "%s: world %d < 1", what, sh->world);
+  if (sh->rank < 0 || sh->rank >= sh->world)
+    return fail(RA_ERR_INVALID_ARG, "%s: rank %d not in [0, %d)", what, sh->rank, sh->world);
+  if (sh->global_len < 0) return fail(RA_ERR_INVALID_ARG, "%s: negative global_len", what);
+  const int64_t parts = sh->assign == RA_ZIGZAG ? 2 * (int64_t)sh->world : sh->world;
+  if (sh->global_len % parts)
+    return fail(RA_ERR_SHAPE, "%s: global_len %lld not divisible by %lld", what,
+                (long long)sh->global_len, (long long)parts);
+  if (S >= 0 && sh->global_len / sh->world != S)
+    return fail(RA_ERR_SHAPE, "%s: share length %lld != global_len/world = %lld", what, (long long)S,
+                (long long)(sh->global_len / sh->world));
+  return RA_OK;
+}
+
+ra::Pos to_pos(const ra_shard& s) { return ra::make_pos(s.assign, s.world, s.rank, s.global_len); }
+
+// Sizes must fit the kernels' 32-bit row indices.
+int check_dims(int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t D) {
+  if (B < 0 || H < 0 || Sq < 0 || Sk < 0 || D < 0) return fail(RA_ERR_INVALID_ARG, "negative size");
+  if (D != 64 && D != 128) return fail(RA_ERR_UNSUPPORTED, "head dim D=%lld not in {64, 128}", (long long)D);
+  const int64_t lim = (int64_t)1 << 30;
+  if (B * H >= lim || Sq >= lim || Sk >= lim)
+    return fail(RA_ERR_UNSUPPORTED, "sizes too large for 32-bit row indexing");
+  return RA_OK;
+}
+
+int launch_attn(const ra::AttnArgs& a, int D, int in_dtype, int o_dtype, hipStream_t stream) {
+  hipError_t e = in_dtype == RA_BF16 ? ra::launch_attn_bf16(a, D, o_dtype, stream)
+                                     : ra::launch_attn_f32(a, D, o_dtype, stream);
+  if (e != hipSuccess) return fail(RA_ERR_HIP, "attention launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* ra_last_error(void) { return g_err; }
+
+int ra_tile_shape(int in_dtype, int64_t D, int64_t* block_m, int64_t* block_n) {
+  if (!block_m || !block_n) return fail(RA_ERR_INVALID_ARG, "ra_tile_shape: NULL output");
+  if (!dtype_ok(in_dtype)) return fail(RA_ERR_UNSUPPORTED, "ra_tile_shape: bad dtype %d", in_dtype);
+  if (D != 64 && D != 128) return fail(RA_ERR_UNSUPPORTED, "ra_tile_shape: D=%lld", (long long)D);
+  *block_m = in_dtype == RA_BF16 ? ra::kBf16BlockM : ra::kF32BlockM;
+  *block_n = in_dtype == RA_BF16 ? ra::kBf16BlockN : ra::kF32BlockN;
+  return ok();
+}
+
+int ra_block_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
+                      int64_t H, int64_t Sq, int64_t Sk, int64_t D, int in_dtype, int o_dtype,
+                      int causal, const ra_shard* q_sh, const ra_shard* kv_sh, float scale,
+                      hipStream_t stream) {
+  int rc = check_dims(B, H, Sq, Sk, D);
+  if (rc) return rc;
+  if (!dtype_ok(in_dtype) || !dtype_ok(o_dtype))
+    return fail(RA_ERR_UNSUPPORTED, "dtype (%d, %d) not RA_F32/RA_BF16", in_dtype, o_dtype);
+  if (causal) {
+    if ((rc = check_shard(q_sh, Sq, "q_sh"))) return rc;
+    if ((rc = check_shard(kv_sh, Sk, "kv_sh"))) return rc;
+  }
+  if (isnan(scale) || isinf(scale)) return fail(RA_ERR_INVALID_ARG, "scale is not finite");
+  const bool empty = B == 0 || H == 0 || Sq == 0;
+  if (!empty) {
+    if (!q || !o || !lse || (Sk > 0 && (!k || !v))) return fail(RA_ERR_INVALID_ARG, "NULL tensor pointer");
+    if (misaligned(q) || misaligned(o) || misaligned(lse) || (Sk > 0 && (misaligned(k) || misaligned(v))))
+      return fail(RA_ERR_MISALIGNED, "tensor pointer not 16-byte aligned");
+  }
+  if (empty) return ok();
+
+  ra::AttnArgs a;
+  memset(&a, 0, sizeof a);
+  a.q = q;
+  a.k[0] = k;
+  a.v[0] = v;
+  a.o = o;
+  a.lse = lse;
+  a.B = (int32_t)B;
+  a.H = (int32_t)H;
+  a.Sq = (int32_t)Sq;
+  a.Sk = (int32_t)Sk;
+  a.nsteps = Sk > 0 ? 1 : 0;
+  a.causal = causal ? 1 : 0;
+  a.store_final = 1;
+  a.scale = scale > 0.f ? scale : (float)(1.0 / sqrt((double)D));
+  if (causal) {
+    a.qpos = to_pos(*q_sh);
+    a.kv_assign = kv_sh->assign;
+    a.kv_world = kv_sh->world;
+    a.kv_len = kv_sh->global_len;
+    a.kv_rank[0] = kv_sh->rank;
+  }
+  return launch_attn(a, (int)D, in_dtype, o_dtype, stream);
+}
+
+size_t ra_ring_share_workspace_bytes(int64_t B, int64_t H, int64_t S_loc, int64_t D) {
+  if (B < 0 || H < 0 || S_loc < 0 || D < 0) return 0;
+  return (size_t)4 * (size_t)(B * S_loc * H * D + 2 * B * H * S_loc);
+}
+
+int ra_ring_share(const void* q, const void* const* k_shares, const void* const* v_shares, void* o,
+                  float* lse, int64_t B, int64_t H, int64_t S_loc, int64_t D, int N, int rank,
+                  int assign, int causal, int in_dtype, int o_dtype, float scale, int start_step,
+                  int num_steps, void* ws, size_t ws_bytes, hipStream_t stream) {
+  int rc = check_dims(B, H, S_loc, S_loc, D);
+  if (rc) return rc;
+  if (!dtype_ok(in_dtype) || !dtype_ok(o_dtype))
+    return fail(RA_ERR_UNSUPPORTED, "dtype (%d, %d) not RA_F32/RA_BF16", in_dtype, o_dtype);
+  if (N < 1) return fail(RA_ERR_INVALID_ARG, "ring size N=%d < 1", N);
+  if (N > RA_MAX_WORLD) return fail(RA_ERR_UNSUPPORTED, "ring size N=%d > %d", N, RA_MAX_WORLD);
+  if (rank < 0 || rank >= N) return fail(RA_ERR_INVALID_ARG, "rank %d not in [0, %d)", rank, N);
+  if (assign < RA_CONTIGUOUS || assign > RA_ZIGZAG) return fail(RA_ERR_INVALID_ARG, "unknown assignment %d", assign);
+  if (start_step < 0 || num_steps < 1 || start_step + num_steps > N)
+    return fail(RA_ERR_INVALID_ARG, "step range [%d, %d) not inside [0, %d] or empty", start_step,
+                start_step + num_steps, N);
+  if (isnan(scale) || isinf(scale)) return fail(RA_ERR_INVALID_ARG, "scale is not finite");
+  const int64_t L = (int64_t)N * S_loc;
+  if (causal && assign == RA_ZIGZAG && S_loc % 2)
+    return fail(RA_ERR_SHAPE, "zigzag needs L %% 2N == 0 (S_loc=%lld is odd)", (long long)S_loc);
+  const bool load_state = start_step > 0;
+  const bool store_final = start_step + num_steps == N;
+  const bool empty = B == 0 || H == 0 || S_loc == 0;
+  if (!empty) {
+    if (!q || !k_shares || !v_shares) return fail(RA_ERR_INVALID_ARG, "NULL q or share array");
+    for (int i = 0; i < N; ++i) {
+      if (!k_shares[i] || !v_shares[i]) return fail(RA_ERR_INVALID_ARG, "share %d pointer is NULL", i);
+      if (misaligned(k_shares[i]) || misaligned(v_shares[i]))
+        return fail(RA_ERR_MISALIGNED, "share %d pointer not 16-byte aligned", i);
+    }
+    if (misaligned(q)) return fail(RA_ERR_MISALIGNED, "q not 16-byte aligned");
+    if (store_final) {
+      if (!o || !lse) return fail(RA_ERR_INVALID_ARG, "NULL o or lse");
+      if (misaligned(o) || misaligned(lse)) return fail(RA_ERR_MISALIGNED, "o/lse not 16-byte aligned");
+    }
+    if (load_state || !store_final) {
+      if (!ws) return fail(RA_ERR_INVALID_ARG, "workspace needed to %s the running state",
+                           load_state ? "resume" : "keep");
+      if (misaligned(ws)) return fail(RA_ERR_MISALIGNED, "workspace not 16-byte aligned");
+      if (ws_bytes < ra_ring_share_workspace_bytes(B, H, S_loc, D))
+        return fail(RA_ERR_INVALID_ARG, "workspace %zu bytes < %zu needed", ws_bytes,
+                    ra_ring_share_workspace_bytes(B, H, S_loc, D));
+    }
+  }
+  if (empty) return ok();
+
+  ra::AttnArgs a;
+  memset(&a, 0, sizeof a);
+  a.q = q;
+  for (int st = 0; st < num_steps; ++st) {
+    // Ring order ([Digest] §3.1/§3.3): at step s the rank holds the KV of rank (rank - s) mod N.
+    const int s = start_step + st;
+    const int src = ((rank - s) % N + N) % N;
+    a.k[st] = k_shares[src];
+    a.v[st] = v_shares[src];
+    a.kv_rank[st] = src;
+  }
+  a.o = o;
+  a.lse = lse;
+  if (ws) {
+    float* w = (float*)ws;
+    a.ws_o = w;
+    a.ws_m = w + B * S_loc * H * D;
+    a.ws_l = a.ws_m + B * H * S_loc;
+  }
+  a.B = (int32_t)B;
+  a.H = (int32_t)H;
+  a.Sq = (int32_t)S_loc;
+  a.Sk = (int32_t)S_loc;
+  a.nsteps = num_steps;
+  a.causal = causal ? 1 : 0;
+  a.load_state = load_state ? 1 : 0;
+  a.store_final = store_final ? 1 : 0;
+  a.scale = scale > 0.f ? scale : (float)(1.0 / sqrt((double)D));
+  a.qpos = ra::make_pos(assign, N, rank, L);
+  a.kv_assign = assign;
+  a.kv_world = N;
+  a.kv_len = L;
+  return launch_attn(a, (int)D, in_dtype, o_dtype, stream);
+}
+
+int ra_lse_merge(void* o_acc, float* lse_acc, const void* o_blk, const float* lse_blk, int64_t B,
+                 int64_t H, int64_t S, int64_t D, int acc_dtype, int blk_dtype, hipStream_t stream) {
+  if (B < 0 || H < 0 || S < 0 || D < 0) return fail(RA_ERR_INVALID_ARG, "negative size");
+  if (!dtype_ok(acc_dtype) || !dtype_ok(blk_dtype))
+    return fail(RA_ERR_UNSUPPORTED, "dtype (%d, %d) not RA_F32/RA_BF16", acc_dtype, blk_dtype);
+  if (D == 0 || D % 8) return fail(RA_ERR_UNSUPPORTED, "D=%lld must be a positive multiple of 8", (long long)D);
+  if (B * S * H == 0) return ok();
+  if (!o_acc || !lse_acc || !o_blk || !lse_blk) return fail(RA_ERR_INVALID_ARG, "NULL tensor pointer");
+  if (misaligned(o_acc) || misaligned(o_blk) || ((uintptr_t)lse_acc & 3) || ((uintptr_t)lse_blk & 3))
+    return fail(RA_ERR_MISALIGNED, "tensor pointer misaligned");
+  hipError_t e = ra::launch_lse_merge(o_acc, lse_acc, o_blk, lse_blk, B, H, S, D, acc_dtype, blk_dtype, stream);
+  if (e != hipSuccess) return fail(RA_ERR_HIP, "merge launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int ra_seq2head_permute(const void* in, void* out, int64_t B, int64_t P, int64_t S_loc, int64_t H,
+                        int64_t D, int dtype, int dst_rank, int inverse, hipStream_t stream) {
+  if (B < 0 || S_loc < 0 || H < 0 || D < 0) return fail(RA_ERR_INVALID_ARG, "negative size");
+  if (P < 1) return fail(RA_ERR_INVALID_ARG, "P=%lld < 1", (long long)P);
+  if (!dtype_ok(dtype)) return fail(RA_ERR_UNSUPPORTED, "dtype %d not RA_F32/RA_BF16", dtype);
+  if (H % P) return fail(RA_ERR_SHAPE, "P=%lld does not divide H=%lld", (long long)P, (long long)H);
+  if (dst_rank < -1 || dst_rank >= P)
+    return fail(RA_ERR_INVALID_ARG, "dst_rank %d not in [-1, %lld)", dst_rank, (long long)P);
+  if (B * S_loc * H * D == 0) return ok();
+  if (!in || !out) return fail(RA_ERR_INVALID_ARG, "NULL tensor pointer");
+  if (misaligned(in) || misaligned(out)) return fail(RA_ERR_MISALIGNED, "tensor pointer not 16-byte aligned");
+  hipError_t e = ra::launch_permute(in, out, B, P, S_loc, H, D, dtype == RA_BF16 ? 2 : 4, dst_rank,
+                                    inverse ? 1 : 0, stream);
+  if (e != hipSuccess) return fail(RA_ERR_HIP, "permute launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int ra_share_work(const ra_shard* q_sh, const ra_shard* kv_sh, int64_t Sq, int64_t Sk, int causal,
+                  int64_t block_m, int64_t block_n, int64_t out[4]) {
+  if (!out) return fail(RA_ERR_INVALID_ARG, "NULL output");
+  if (Sq < 0 || Sk < 0 || block_m < 1 || block_n < 1) return fail(RA_ERR_INVALID_ARG, "bad sizes");
+  int rc;
+  if (causal) {
+    if ((rc = check_shard(q_sh, Sq, "q_sh"))) return rc;
+    if ((rc = check_shard(kv_sh, Sk, "kv_sh"))) return rc;
+  }
+  const int64_t n_qt = (Sq + block_m - 1) / block_m;
+  const int64_t n_kt = (Sk + block_n - 1) / block_n;
+  if (!causal) {
+    out[0] = Sq * Sk;
+    out[1] = n_qt * n_kt;
+    out[2] = out[3] = 0;
+    return ok();
+  }
+  const ra::Pos qp = to_pos(*q_sh), kp = to_pos(*kv_sh);
+  int64_t pairs = 0;
+  for (int64_t i = 0; i < Sq; ++i) pairs += ra::clamp64(ra::count_le(kp, ra::pos_of(qp, i)), 0, Sk);
+  int64_t full = 0, partial = 0, skip = 0;
+  for (int64_t t = 0; t < n_qt; ++t) {
+    const int64_t r0 = t * block_m, r1 = (r0 + block_m < Sq ? r0 + block_m : Sq) - 1;
+    const int64_t cmin = ra::clamp64(ra::count_le(kp, ra::pos_of(qp, r0)), 0, Sk);
+    const int64_t cmax = ra::clamp64(ra::count_le(kp, ra::pos_of(qp, r1)), 0, Sk);
+    // Tiles made only of keys visible to the tile's first (smallest-position) row are full.
+    const int64_t nfull = cmin / block_n + ((cmin == Sk && Sk % block_n) ? 1 : 0);
+    const int64_t active = (cmax + block_n - 1) / block_n;
+    full += nfull;
+    partial += active - nfull;
+    skip += n_kt - active;
+  }
+  out[0] = pairs;
+  out[1] = full;
+  out[2] = partial;
+  out[3] = skip;
+  return ok();
+}
+
+int ra_debug_positions(const ra_shard* sh, int64_t* out, hipStream_t stream) {
+  int rc = check_shard(sh, -1, "sh");
+  if (rc) return rc;
+  const int64_t n = sh->global_len / sh->world;
+  if (n == 0) return ok();
+  if (!out) return fail(RA_ERR_INVALID_ARG, "NULL output");
+  hipError_t e = ra::launch_debug_positions(to_pos(*sh), n, out, stream);
+  if (e != hipSuccess) return fail(RA_ERR_HIP, "positions launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int ra_debug_mask(const ra_shard* q_sh, const ra_shard* kv_sh, int64_t Sq, int64_t Sk, uint8_t* out,
+                  hipStream_t stream) {
+  int rc;
+  if ((rc = check_shard(q_sh, Sq, "q_sh"))) return rc;
+  if ((rc = check_shard(kv_sh, Sk, "kv_sh"))) return rc;
+  if (Sq * Sk == 0) return ok();
+  if (!out) return fail(RA_ERR_INVALID_ARG, "NULL output");
+  hipError_t e = ra::launch_debug_mask(to_pos(*q_sh), to_pos(*kv_sh), Sq, Sk, out, stream);
+  if (e != hipSuccess) return fail(RA_ERR_HIP, "mask launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // extern "C"

@@ -8,8 +8,10 @@ path can take their inputs from here without sharing any of the method's
 arithmetic.
 
 Recipe (the pages give none; this is the stated reading):
-  * generator: ``numpy.random.default_rng(seed)`` (PCG64),
-    ``standard_normal(dtype=float32)``, multiplied by ``std``;
+  * generator: numpy PCG64, ``standard_normal(dtype=float32)`` multiplied by ``std``; a
+    tensor is filled in blocks of ``GEN_ROWS`` leading-dimension rows (all dimensions but
+    the first flattened), block ``j`` drawn from ``numpy.random.default_rng([seed, j])``,
+    so blocks can be generated in parallel threads with a fixed result;
   * bf16 inputs are those float32 values rounded to nearest-even bfloat16;
   * a workload's Q, K and V are drawn as one *global* tensor ``[B, L, H, D]``
     each, from seeds ``1000*k + 0, 1, 2`` for workload number ``k``; a rank's
@@ -18,18 +20,48 @@ Recipe (the pages give none; this is the stated reading):
 """
 from __future__ import annotations
 
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 
 from .configs import CONFIGS, Workload, get  # noqa: F401
 
+GEN_ROWS = 4096          # rows of the flattened leading dimension per generator block
+_THREADS = max(1, min(16, os.cpu_count() or 1))
+
+
+def _blocks(shape):
+    shape = tuple(int(x) for x in shape)
+    rows = int(np.prod(shape[:-1])) if len(shape) > 1 else 1
+    inner = shape[-1] if len(shape) > 1 else (shape[0] if shape else 1)
+    return rows, inner
+
+
+def _fill(seed: int, shape, std: float, convert):
+    rows, inner = _blocks(shape)
+    out = np.empty((rows, inner), dtype=np.uint16 if convert else np.float32)
+    nblk = (rows + GEN_ROWS - 1) // GEN_ROWS
+
+    def work(j):
+        r0, r1 = j * GEN_ROWS, min(rows, (j + 1) * GEN_ROWS)
+        x = np.random.default_rng([seed, j]).standard_normal(size=(r1 - r0, inner), dtype=np.float32)
+        if std != 1.0:
+            x *= np.float32(std)
+        out[r0:r1] = f32_to_bf16_bits(x) if convert else x
+
+    if nblk <= 1:
+        for j in range(nblk):
+            work(j)
+    else:
+        with ThreadPoolExecutor(_THREADS) as ex:
+            list(ex.map(work, range(nblk)))
+    return out.reshape(shape)
+
 
 def gaussian_f32(seed: int, shape, std: float = 1.0) -> np.ndarray:
-    """float32 array of iid N(0, std^2) values from PCG64 seeded with ``seed``."""
-    rng = np.random.default_rng(seed)
-    x = rng.standard_normal(size=shape, dtype=np.float32)
-    if std != 1.0:
-        x *= np.float32(std)
-    return x
+    """float32 array of iid N(0, std^2) values (see the module recipe)."""
+    return _fill(seed, shape, std, convert=False)
 
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -41,10 +73,11 @@ def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     x = np.ascontiguousarray(x, dtype=np.float32)
     if not np.all(np.isfinite(x)):
         raise ValueError("f32_to_bf16_bits: non-finite input")
-    u = x.view(np.uint32).astype(np.uint64)
-    lsb = (u >> np.uint64(16)) & np.uint64(1)
-    u = (u + np.uint64(0x7FFF) + lsb) >> np.uint64(16)
-    return u.astype(np.uint16)
+    u = x.view(np.uint32).copy()
+    lsb = (u >> np.uint32(16)) & np.uint32(1)
+    u += np.uint32(0x7FFF)   # finite inputs stay below 2^32 after both additions
+    u += lsb
+    return (u >> np.uint32(16)).astype(np.uint16)
 
 
 def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
@@ -55,7 +88,7 @@ def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
 
 def gaussian_bf16_bits(seed: int, shape, std: float = 1.0) -> np.ndarray:
     """uint16 bfloat16 bit patterns of iid N(0, std^2) draws (see module recipe)."""
-    return f32_to_bf16_bits(gaussian_f32(seed, shape, std))
+    return _fill(seed, shape, std, convert=True)
 
 
 def global_qkv(w: "Workload"):

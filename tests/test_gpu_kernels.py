@@ -1,0 +1,241 @@
+"""GPU parity of every entry point against the fp64 oracle, at sizes the oracle finishes in
+seconds (several tiles, ragged tails, every assignment, empty rows, both dtypes)."""
+import numpy as np
+import pytest
+import torch
+
+from gpu_helpers import TOL, check, dev, gen, half_ulp_bf16, host, say, shares, values
+from oracle import attention as OA
+from oracle import permute as OU
+from oracle import positions as OP
+from oracle import ring as OR
+
+pytestmark = pytest.mark.gpu
+
+ra = pytest.importorskip("ring_sequence_parallelism_ra_amd")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    torch.cuda.set_device(0)
+
+
+ASSIGNS = ["contiguous", "striped", "zigzag"]
+
+
+@pytest.mark.parametrize("assign", ASSIGNS)
+@pytest.mark.parametrize("n,l", [(1, 64), (4, 256), (8, 8192), (8, 262144), (3, 600)])
+def test_positions_bit_exact(assign, n, l):
+    if assign == "zigzag" and l % (2 * n):
+        pytest.skip("zigzag needs L % 2N == 0")
+    for r in range(n):
+        got = ra.debug_positions(ra.Shard(assign, n, r, l)).cpu().numpy()
+        assert np.array_equal(got, OP.positions(assign, n, r, l))
+
+
+@pytest.mark.parametrize("assign", ASSIGNS)
+def test_mask_bit_exact(assign):
+    n, l = 4, 512
+    s = l // n
+    for r in range(n):
+        for src in range(n):
+            got = ra.debug_mask(ra.Shard(assign, n, r, l), ra.Shard(assign, n, src, l), s, s).cpu().numpy()
+            want = OA.visible(OP.positions(assign, n, r, l), OP.positions(assign, n, src, l), True)
+            assert np.array_equal(got.astype(bool), want), (r, src)
+
+
+BLOCK_CASES = [
+    # (causal, assign, N, L, q_rank, kv_rank, Sq, Sk) ; non-causal cases use Sq/Sk directly
+    (False, None, 0, 0, 0, 0, 300, 200),
+    (False, None, 0, 0, 0, 0, 1, 1),
+    (False, None, 0, 0, 0, 0, 130, 1000),
+    (False, None, 0, 0, 0, 0, 64, 64),
+    (True, "contiguous", 4, 1200, 2, 2, 300, 300),
+    (True, "contiguous", 4, 1200, 3, 1, 300, 300),
+    (True, "striped", 3, 600, 1, 2, 200, 200),
+    (True, "striped", 3, 600, 2, 0, 200, 200),
+    (True, "zigzag", 2, 520, 0, 1, 260, 260),
+    (True, "zigzag", 2, 520, 1, 0, 260, 260),
+    (True, "contiguous", 1, 333, 0, 0, 333, 333),
+]
+
+
+@pytest.mark.parametrize("case", BLOCK_CASES, ids=[f"c{i}" for i in range(len(BLOCK_CASES))])
+@pytest.mark.parametrize("in_dt,o_dt", [("bf16", "bf16"), ("bf16", "f32"), ("f32", "f32"), ("f32", "bf16")])
+@pytest.mark.parametrize("d", [128, 64])
+def test_block_attn_parity(case, in_dt, o_dt, d):
+    causal, assign, n, l, qr, kr, sq, sk = case
+    b, h = 2, 3
+    seed = 17 + sq + 3 * sk + d
+    say(f"block_attn case={case} in={in_dt} out={o_dt} D={d} seed={seed}")
+    q, k, v = gen(seed, (b, sq, h, d), in_dt), gen(seed + 1, (b, sk, h, d), in_dt), gen(seed + 2, (b, sk, h, d), in_dt)
+    qs = ks = None
+    qpos = kpos = None
+    if causal:
+        qs, ks = ra.Shard(assign, n, qr, l), ra.Shard(assign, n, kr, l)
+        qpos, kpos = OP.positions(assign, n, qr, l), OP.positions(assign, n, kr, l)
+    o, lse = ra.block_attn_fwd(dev(q, in_dt), dev(k, in_dt), dev(v, in_dt), causal=causal, q_shard=qs, kv_shard=ks,
+                               out_dtype=torch.bfloat16 if o_dt == "bf16" else torch.float32)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = OA.attention(values(q, in_dt), values(k, in_dt), values(v, in_dt), qpos, kpos, causal)
+    check(o, lse, o_ref, lse_ref, in_dt, o_dt, what=str(case))
+
+
+@pytest.mark.parametrize("in_dt", ["bf16", "f32"])
+def test_block_attn_all_rows_empty(in_dt):
+    # contiguous rank 0's queries precede every key of rank 3: no visible key at all
+    n, l = 4, 512
+    s = l // n
+    q, k, v = (gen(i, (1, s, 2, 128), in_dt) for i in (1, 2, 3))
+    o, lse = ra.block_attn_fwd(dev(q, in_dt), dev(k, in_dt), dev(v, in_dt), causal=True,
+                               q_shard=ra.Shard("contiguous", n, 0, l), kv_shard=ra.Shard("contiguous", n, 3, l))
+    torch.cuda.synchronize()
+    assert torch.all(o.float() == 0) and torch.all(torch.isneginf(lse))
+
+
+@pytest.mark.parametrize("in_dt", ["bf16", "f32"])
+def test_block_attn_scale(in_dt):
+    sq = sk = 96
+    q, k, v = (gen(40 + i, (1, sq, 2, 64), in_dt) for i in range(3))
+    o, lse = ra.block_attn_fwd(dev(q, in_dt), dev(k, in_dt), dev(v, in_dt), scale=0.3)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = OA.attention(values(q, in_dt), values(k, in_dt), values(v, in_dt), scale=0.3)
+    check(o, lse, o_ref, lse_ref, in_dt, in_dt, "scale=0.3")
+
+
+RING_CASES = [
+    ("contiguous", 4, 4 * 200), ("striped", 4, 4 * 200), ("zigzag", 4, 4 * 200),
+    ("contiguous", 8, 8 * 130), ("striped", 8, 8 * 136), ("zigzag", 8, 8 * 130),
+    ("zigzag", 2, 2 * 384), ("striped", 1, 300), ("contiguous", 3, 3 * 128),
+]
+
+
+@pytest.mark.parametrize("case", RING_CASES, ids=[f"{a}-N{n}-L{l}" for a, n, l in RING_CASES])
+@pytest.mark.parametrize("in_dt", ["bf16", "f32"])
+@pytest.mark.parametrize("causal", [True, False])
+def test_ring_share_parity(case, in_dt, causal):
+    assign, n, l = case
+    b, h, d = 1, 2, 128
+    seed = 100 + n + l
+    say(f"ring_share {case} in={in_dt} causal={causal} seed={seed}")
+    gq, gk, gv = (gen(seed + i, (b, l, h, d), in_dt) for i in range(3))
+    qs, ks, vs = shares(gq, assign, n), shares(gk, assign, n), shares(gv, assign, n)
+    kd = [dev(x, in_dt) for x in ks]
+    vd = [dev(x, in_dt) for x in vs]
+    kv_full, vv_full = values(gk, in_dt), values(gv, in_dt)
+    for r in range(n):
+        o, lse = ra.ring_share(dev(qs[r], in_dt), kd, vd, r, assign=assign, causal=causal)
+        torch.cuda.synchronize()
+        qpos = OP.positions(assign, n, r, l)
+        o_ref, lse_ref = OA.attention(values(qs[r], in_dt), kv_full, vv_full, qpos, np.arange(l), causal)
+        check(o, lse, o_ref, lse_ref, in_dt, in_dt, what=f"rank {r}")
+
+
+@pytest.mark.parametrize("in_dt", ["bf16", "f32"])
+@pytest.mark.parametrize("assign", ASSIGNS)
+def test_ring_share_split_and_resume(in_dt, assign):
+    # The state after any prefix of the steps is complete: [0,k) then [k,N), or one step per
+    # call, reaches the one-call result (order/block independence, Digest §3.2).
+    n, l, b, h, d = 4, 4 * 192, 1, 2, 64
+    gq, gk, gv = (gen(300 + i, (b, l, h, d), in_dt) for i in range(3))
+    qs, ks, vs = shares(gq, assign, n), shares(gk, assign, n), shares(gv, assign, n)
+    kd = [dev(x, in_dt) for x in ks]
+    vd = [dev(x, in_dt) for x in vs]
+    r = 2
+    qd = dev(qs[r], in_dt)
+    o1, lse1 = ra.ring_share(qd, kd, vd, r, assign=assign)
+    ws = ra.ring_share_workspace(b, h, l // n, d)
+    ra.ring_share(qd, kd, vd, r, assign=assign, start_step=0, num_steps=1, ws=ws)
+    o2, lse2 = ra.ring_share(qd, kd, vd, r, assign=assign, start_step=1, num_steps=3, ws=ws)
+    for st in range(n - 1):
+        ra.ring_share(qd, kd, vd, r, assign=assign, start_step=st, num_steps=1, ws=ws)
+    o3, lse3 = ra.ring_share(qd, kd, vd, r, assign=assign, start_step=n - 1, num_steps=1, ws=ws)
+    torch.cuda.synchronize()
+    qpos = OP.positions(assign, n, r, l)
+    o_ref, lse_ref = OA.attention(values(qs[r], in_dt), values(gk, in_dt), values(gv, in_dt), qpos, np.arange(l), True)
+    for o, lse in ((o1, lse1), (o2, lse2), (o3, lse3)):
+        check(o, lse, o_ref, lse_ref, in_dt, in_dt, what="split")
+
+
+@pytest.mark.parametrize("acc_dt,blk_dt", [("f32", "f32"), ("f32", "bf16"), ("bf16", "f32"), ("bf16", "bf16")])
+@pytest.mark.parametrize("d", [128, 64, 8])
+def test_lse_merge_parity(acc_dt, blk_dt, d):
+    b, s, h = 2, 77, 3
+    rng = np.random.default_rng(d)
+    oa, ob = gen(500 + d, (b, s, h, d), acc_dt), gen(600 + d, (b, s, h, d), blk_dt)
+    la = rng.standard_normal((b, h, s)).astype(np.float32) * 5
+    lb = rng.standard_normal((b, h, s)).astype(np.float32) * 5
+    la[0, 0, :5] = -np.inf
+    lb[0, 0, 3:8] = -np.inf     # rows 3, 4 are empty on both sides
+    lb[1, 2, 10] = la[1, 2, 10]  # a tie
+    oad, lad = dev(oa, acc_dt), torch.from_numpy(la).cuda()
+    ra.lse_merge(oad, lad, dev(ob, blk_dt), torch.from_numpy(lb).cuda())
+    torch.cuda.synchronize()
+    o_ref, l_ref = OR.lse_merge(values(oa, acc_dt), np.transpose(la, (0, 2, 1)), values(ob, blk_dt),
+                                np.transpose(lb, (0, 2, 1)))
+    l_ref = np.transpose(l_ref, (0, 2, 1))
+    bound = 2e-6 + (half_ulp_bf16(o_ref) if acc_dt == "bf16" else 0.0)
+    assert np.all(np.abs(host(oad) - o_ref) <= bound)
+    got_l = host(lad)
+    assert np.array_equal(np.isneginf(got_l), np.isneginf(l_ref))
+    fin = np.isfinite(l_ref)
+    assert np.max(np.abs(got_l[fin] - l_ref[fin])) <= 2e-6
+    assert np.all(host(oad)[0, 3:5, 0] == 0)
+
+
+@pytest.mark.parametrize("p", [2, 4, 8])
+@pytest.mark.parametrize("hmul", [1, 2])
+@pytest.mark.parametrize("s", [1, 3, 64])
+@pytest.mark.parametrize("d,dt", [(128, "bf16"), (64, "bf16"), (64, "f32"), (1, "bf16"), (3, "f32")])
+def test_permute_bit_exact(p, hmul, s, d, dt):
+    h, b = p * hmul, 2
+    x = gen(700 + p + s + d, (p, b, s, h, d), dt)
+    xd = dev(x, dt)
+    for dst in (0, p - 1, -1):
+        y = ra.seq2head_permute(xd, dst)
+        torch.cuda.synchronize()
+        want = OU.seq2head(x, dst)
+        got = y.cpu().view(torch.int16 if dt == "bf16" else torch.int32).numpy()
+        assert np.array_equal(got, want.view(np.int16 if dt == "bf16" else np.int32))
+        fill = np.full_like(x, 0x3f80 if dt == "bf16" else 7)
+        out = dev(fill, dt)
+        ra.head2seq_permute(y, dst, out)
+        torch.cuda.synchronize()
+        want_back = OU.head2seq(want, dst, fill.copy())
+        got_back = out.cpu().view(torch.int16 if dt == "bf16" else torch.int32).numpy()
+        assert np.array_equal(got_back, want_back.view(np.int16 if dt == "bf16" else np.int32))
+
+
+def test_future_keys_never_read():
+    # Keys later than every query of the share are invisible: filling them with +-1e4 garbage
+    # must leave O and LSE bit-identical (tile skipping and masking together).
+    assign, n, l, b, h, d = "striped", 4, 1024, 1, 2, 128
+    gq, gk, gv = (gen(900 + i, (b, l, h, d), "bf16") for i in range(3))
+    r = 1
+    qpos = OP.positions(assign, n, r, l)
+    qs = shares(gq, assign, n)
+    o1, lse1 = ra.ring_share(dev(qs[r], "bf16"), [dev(x, "bf16") for x in shares(gk, assign, n)],
+                             [dev(x, "bf16") for x in shares(gv, assign, n)], r, assign=assign)
+    for x in (gk, gv):
+        late = np.arange(l) > qpos.max()
+        junk = np.where(np.random.default_rng(0).random(x[:, late].shape) < 0.5, 0x461C, 0xC61C)  # +-1e4
+        x[:, late] = junk.astype(np.uint16)
+    o2, lse2 = ra.ring_share(dev(qs[r], "bf16"), [dev(x, "bf16") for x in shares(gk, assign, n)],
+                             [dev(x, "bf16") for x in shares(gv, assign, n)], r, assign=assign)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(lse1.view(torch.int32), lse2.view(torch.int32))
+
+
+def test_deterministic():
+    assign, n, l = "zigzag", 8, 8 * 256
+    gq, gk, gv = (gen(950 + i, (1, l, 4, 128), "bf16") for i in range(3))
+    kd = [dev(x, "bf16") for x in shares(gk, assign, n)]
+    vd = [dev(x, "bf16") for x in shares(gv, assign, n)]
+    qd = dev(shares(gq, assign, n)[5], "bf16")
+    o1, l1 = ra.ring_share(qd, kd, vd, 5, assign=assign)
+    o2, l2 = ra.ring_share(qd, kd, vd, 5, assign=assign)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
