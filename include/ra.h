@@ -104,7 +104,8 @@ int ra_lse_merge(void* o_acc, float* lse_acc, const void* o_blk, const float* ls
                  hipStream_t stream);
 
 /* Bytes of workspace ra_ring_share needs to keep the running state between calls:
- * fp32 O [B, S, H, D] plus fp32 running max and running sum [B, H, S] each. */
+ * un-normalised fp32 O [B, S, H, D], then the running max and the running sum [B, H, S]
+ * each in 8-byte (fp64) slots. */
 size_t ra_ring_share_workspace_bytes(int64_t B, int64_t H, int64_t S_loc, int64_t D);
 
 /*

@@ -158,8 +158,8 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(const AttnArgs a) {
   const int64_t state_row = ((int64_t)b * a.H + h) * a.Sq + qrow;          // [B, H, S]
   const int64_t out_row = (((int64_t)b * a.Sq + qrow) * a.H + h) * D;       // [B, S, H, D]
   if (a.load_state && qvalid) {
-    m_run = a.ws_m[state_row];
-    l_run = hh == 0 ? a.ws_l[state_row] : 0.f;
+    m_run = (float)a.ws_m[state_row];  // stored from this kernel's own fp32 values: exact
+    l_run = hh == 0 ? (float)a.ws_l[state_row] : 0.f;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll

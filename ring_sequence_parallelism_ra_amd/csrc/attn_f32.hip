@@ -4,8 +4,9 @@
 // 再到 USP 统一框架": definition §2, ring order §3.1/§3.3, update §3.2, causal matrix §3.4)
 // for the small fp32 checks, where accuracy matters and speed does not. One lane owns one
 // query row; a wave64 workgroup owns 64 rows of one (batch, head). K/V tiles of 32 keys
-// are staged in LDS and read by every lane as broadcasts. The softmax runs in the natural
-// exp domain with the accurate device-library expf/logf.
+// are staged in LDS and read by every lane as broadcasts. Logits, the running max and sum and
+// the LSE are carried in fp64 (exact products of the fp32 inputs, device-library exp/log in
+// double), so the only fp32 rounding of the LSE is the final store; O accumulates in fp32.
 #include <math.h>
 
 #include "ra_internal.h"
@@ -44,7 +45,8 @@ __global__ __launch_bounds__(BM) void attn_f32_kernel(const AttnArgs a) {
     if (qvalid) my_qpos = pos_of(a.qpos, qrow);
   }
 
-  float m_run = -INFINITY, l_run = 0.f;
+  double m_run = -INFINITY, l_run = 0.0;
+  const double scale = a.scale;
   float o[D];
 #pragma unroll
   for (int d = 0; d < D; ++d) o[d] = 0.f;
@@ -52,7 +54,7 @@ __global__ __launch_bounds__(BM) void attn_f32_kernel(const AttnArgs a) {
   const int64_t out_row = (((int64_t)b * a.Sq + qrow) * a.H + h) * D;
   if (a.load_state && qvalid) {
     m_run = a.ws_m[state_row];
-    l_run = a.ws_l[state_row];
+    l_run = a.ws_l[state_row];  // fp64 state slots
 #pragma unroll
     for (int d = 0; d < D; ++d) o[d] = a.ws_o[out_row + d];
   }
@@ -72,49 +74,51 @@ __global__ __launch_bounds__(BM) void attn_f32_kernel(const AttnArgs a) {
         vs_[u] = key < a.Sk ? vb[key * rs + d] : 0.f;
       }
       __syncthreads();
-      float sc[BN];
-      float mt = -INFINITY;
+      double sc[BN];
+      double mt = -INFINITY;
       for (int j = 0; j < BN; ++j) {
-        float acc0 = 0.f, acc1 = 0.f, acc2 = 0.f, acc3 = 0.f;
+        double acc0 = 0.0, acc1 = 0.0, acc2 = 0.0, acc3 = 0.0;
 #pragma unroll 8
         for (int d = 0; d < D; d += 4) {
-          acc0 = fmaf(q[d + 0], ks_[j * D + d + 0], acc0);
-          acc1 = fmaf(q[d + 1], ks_[j * D + d + 1], acc1);
-          acc2 = fmaf(q[d + 2], ks_[j * D + d + 2], acc2);
-          acc3 = fmaf(q[d + 3], ks_[j * D + d + 3], acc3);
+          acc0 = fma((double)q[d + 0], (double)ks_[j * D + d + 0], acc0);
+          acc1 = fma((double)q[d + 1], (double)ks_[j * D + d + 1], acc1);
+          acc2 = fma((double)q[d + 2], (double)ks_[j * D + d + 2], acc2);
+          acc3 = fma((double)q[d + 3], (double)ks_[j * D + d + 3], acc3);
         }
-        float sj = ((acc0 + acc1) + (acc2 + acc3)) * a.scale;
+        double sj = ((acc0 + acc1) + (acc2 + acc3)) * scale;
         const int key = key0 + j;
         bool vis = key < a.Sk;
         if (a.causal) vis = vis && visible(my_qpos, pos_of(kvp, key));
         sj = vis ? sj : -INFINITY;
         sc[j] = sj;
-        mt = fmaxf(mt, sj);
+        mt = fmax(mt, sj);
       }
-      const float m_new = fmaxf(m_run, mt);
-      const float base = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = expf(m_run - base);
+      const double m_new = fmax(m_run, mt);
+      const double base = m_new == -INFINITY ? 0.0 : m_new;
+      const double alpha = exp(m_run - base);
       m_run = m_new;
       l_run *= alpha;
+      const float alpha_f = (float)alpha;
 #pragma unroll
-      for (int d = 0; d < D; ++d) o[d] *= alpha;
+      for (int d = 0; d < D; ++d) o[d] *= alpha_f;
       for (int j = 0; j < BN; ++j) {
-        const float p = expf(sc[j] - base);
+        const double p = exp(sc[j] - base);
         l_run += p;
+        const float pf = (float)p;
 #pragma unroll
-        for (int d = 0; d < D; ++d) o[d] = fmaf(p, vs_[j * D + d], o[d]);
+        for (int d = 0; d < D; ++d) o[d] = fmaf(pf, vs_[j * D + d], o[d]);
       }
     }
   }
 
   if (!qvalid) return;
   if (a.store_final) {
-    const bool any = l_run > 0.f;
-    const float inv = any ? 1.f / l_run : 0.f;
+    const bool any = l_run > 0.0;
+    const double inv = any ? 1.0 / l_run : 0.0;
     OutT* op = (OutT*)a.o + out_row;
 #pragma unroll
-    for (int d = 0; d < D; ++d) op[d] = (OutT)(o[d] * inv);
-    a.lse[state_row] = any ? m_run + logf(l_run) : -INFINITY;
+    for (int d = 0; d < D; ++d) op[d] = (OutT)(float)(o[d] * inv);
+    a.lse[state_row] = any ? (float)(m_run + log(l_run)) : -INFINITY;
   } else {
 #pragma unroll
     for (int d = 0; d < D; ++d) a.ws_o[out_row + d] = o[d];

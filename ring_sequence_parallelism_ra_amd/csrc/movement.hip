@@ -73,15 +73,18 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(void* __restrict__ o_acc
   const int64_t s = (row / H) % S;
   const int64_t b = row / (H * S);
   const int64_t li = (b * H + h) * S + s;
-  const float la = lse_acc[li];
-  const float lb = lse_blk[li];
+  // The LSE arithmetic runs in fp64 on the fp32 inputs so that the merged LSE is rounded
+  // once, at the store.
+  const double la = lse_acc[li];
+  const double lb = lse_blk[li];
   const bool fa = la != -INFINITY, fb = lb != -INFINITY;
-  float lse, wa, wb;
+  double lse;
+  float wa, wb;
   if (fa && fb) {
-    const float hi = fmaxf(la, lb);
-    lse = hi + log1pf(expf(-fabsf(la - lb)));
-    wa = expf(la - lse);
-    wb = expf(lb - lse);
+    const double hi = fmax(la, lb);
+    lse = hi + log1p(exp(-fabs(la - lb)));
+    wa = (float)exp(la - lse);
+    wb = (float)exp(lb - lse);
   } else if (fa) {
     lse = la, wa = 1.f, wb = 0.f;
   } else if (fb) {
@@ -97,7 +100,7 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(void* __restrict__ o_acc
 #pragma unroll
   for (int i = 0; i < 8; ++i) y[i] = (wa == 0.f ? 0.f : xa[i] * wa) + (wb == 0.f ? 0.f : xb[i] * wb);
   Vec8<TA>::store(o_acc, off, y);
-  if (chunk == 0) lse_acc[li] = lse;
+  if (chunk == 0) lse_acc[li] = (float)lse;
 }
 
 // Sequence-sharded [P, B, S, H, D] <-> head-sharded [B, P*S, H/P, D] (per destination rank).

@@ -131,7 +131,7 @@ int ra_block_attn_fwd(const void* q, const void* k, const void* v, void* o, floa
 
 size_t ra_ring_share_workspace_bytes(int64_t B, int64_t H, int64_t S_loc, int64_t D) {
   if (B < 0 || H < 0 || S_loc < 0 || D < 0) return 0;
-  return (size_t)4 * (size_t)(B * S_loc * H * D + 2 * B * H * S_loc);
+  return (size_t)4 * (size_t)(B * S_loc * H * D) + (size_t)16 * (size_t)(B * H * S_loc);
 }
 
 int ra_ring_share(const void* q, const void* const* k_shares, const void* const* v_shares, void* o,
@@ -193,9 +193,11 @@ int ra_ring_share(const void* q, const void* const* k_shares, const void* const*
   a.o = o;
   a.lse = lse;
   if (ws) {
+    // [B, S, H, D] fp32 O, then [B, H, S] fp64 running max, then [B, H, S] fp64 running sum.
+    // The O part is a multiple of 16 bytes (D is 64 or 128), so the fp64 parts stay aligned.
     float* w = (float*)ws;
     a.ws_o = w;
-    a.ws_m = w + B * S_loc * H * D;
+    a.ws_m = (double*)(w + B * S_loc * H * D);
     a.ws_l = a.ws_m + B * H * S_loc;
   }
   a.B = (int32_t)B;

@@ -72,9 +72,9 @@ struct AttnArgs {
   int32_t kv_rank[kMaxSteps];
   void* o;
   float* lse;
-  float* ws_o;  // running state (may be null when neither loaded nor stored)
-  float* ws_m;
-  float* ws_l;
+  float* ws_o;   // running state (may be null when neither loaded nor stored):
+  double* ws_m;  // un-normalised O in fp32, running max and running sum in fp64 slots
+  double* ws_l;
   int32_t B, H, Sq, Sk;
   int32_t nsteps;
   int32_t causal;

@@ -95,7 +95,7 @@ def test_ring_share_validation():
     # partial runs need a workspace of the right size
     assert call_ring(start=0, num=2) == INVALID
     need = lib.ra_ring_share_workspace_bytes(1, 2, 64, 128)
-    assert need == 4 * (64 * 2 * 128 + 2 * 2 * 64)
+    assert need == 4 * 64 * 2 * 128 + 16 * 2 * 64
     assert call_ring(start=1, num=3, ws=FAKE, wsb=need - 4) == INVALID
     assert call_ring(D=64, ind=5) == UNSUP
     assert call_ring(B=0, q=None) == OK
