@@ -12,21 +12,28 @@
 //  * Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16: K tile rows
 //    from LDS are the A operand, the wave's Q rows (held in VGPRs for the whole kernel) are
 //    the B operand. The 32x32 fp32 result leaves each lane with 16 keys of its own query, so
-//    the row max and row sum are in-lane reductions plus one exchange with lane l^32.
+//    the row max and row sum are in-lane reductions plus one v_permlane32_swap.
 //  * O^T += V^T P^T with the same instruction: P^T is the score accumulator converted to
-//    bf16 in place (no data movement), V^T comes from LDS, where the V tile is stored
-//    transposed with bits 2 and 3 of the key index swapped inside each 16-key group, so
-//    that the 8 keys a lane needs are one 16-byte read and match the key order the score
-//    accumulator hands to the B operand.
-//  * K/V tiles (64 keys) are fetched with 128-bit coalesced global loads into registers
-//    one tile ahead and written to the other half of a double-buffered LDS stage, one
-//    barrier per tile.
+//    bf16 in place (no data movement). V stays in LDS in its natural [key][d] layout and the
+//    transposed A operand is read with ds_read_b64_tr_b16, which hands each lane one head-dim
+//    column of a 4-key x 16-column block; two such reads give the 8 keys that match, key for
+//    key, the order in which the score accumulator feeds the B operand.
+//  * K/V tiles (64 keys) go from HBM straight into LDS with global_load_lds_dwordx4 (each
+//    lane moves 16 bytes, a wave 1 KB), so staging costs no registers and no LDS-write
+//    instructions. Rows are unpadded; the 16-byte chunks of each row are XOR-permuted by a
+//    function of the key so that the 128-bit K reads and the transposed V reads hit distinct
+//    banks. The staging is staggered so that, while tile j is in the softmax, K of tile j+1
+//    and V of tile j are resident: the next tile's QK^T MFMAs are issued in the same block as
+//    this tile's softmax VALU work and the two overlap. One barrier per tile.
 //  * Tiles whose keys are all invisible to the workgroup's rows are never visited: the
 //    visible keys of a share form a prefix (positions increase along a share), whose length
 //    comes from the position rule. Only tiles straddling the causal boundary or the ragged
 //    tail evaluate the mask. Workgroups are launched heaviest query tile first.
-//  * Everything in the softmax is kept in the log2 domain (exp2 of scores pre-multiplied by
-//    scale*log2 e); LSE is converted back to natural log at the end.
+//  * The softmax runs in the log2 domain (exp2 of scores pre-multiplied by scale*log2 e).
+//    The running max is only raised when a tile's max exceeds it by more than kLazy (so the
+//    weights stay <= 2^kLazy); the O rescale that goes with it is skipped otherwise. The
+//    result does not depend on the reference value subtracted; LSE is converted back to the
+//    natural log at the end.
 #include <math.h>
 
 #include "ra_internal.h"
@@ -36,29 +43,36 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int BM = kBf16BlockM;   // query rows per workgroup
 constexpr int BN = kBf16BlockN;   // keys per tile
 constexpr int NT = 256;           // threads per workgroup (4 wave64)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kLazy = 8.f;      // max growth (log2 units) absorbed without rescaling O
+#ifndef RA_ATTN_WAVES_PER_SIMD
+#define RA_ATTN_WAVES_PER_SIMD 2      // occupancy target: 256 VGPRs per wave at 2, 512 at 1
+#endif
 
 template <int D>
 struct Cfg {
-  static constexpr int KS = D + 8;                // K tile row stride in LDS (elements)
-  static constexpr int VS = BN + 8;               // V^T tile row stride in LDS
-  static constexpr int K_ELEMS = BN * KS;
-  static constexpr int V_ELEMS = D * VS;
-  static constexpr int STAGE = K_ELEMS + V_ELEMS;
-  static constexpr int KCH = D / 8;               // 16-byte chunks per row
-  static constexpr int K_UNITS = BN * KCH;        // (key, chunk) copies per tile
-  static constexpr int V_UNITS = (BN / 4) * KCH;  // (4-key group, chunk) copies per tile
-  static constexpr int K_PER_T = (K_UNITS + NT - 1) / NT;
-  static constexpr int V_PER_T = (V_UNITS + NT - 1) / NT;
+  static constexpr int ROWB = D * 2;               // bytes per K/V row in LDS (unpadded)
+  static constexpr int SPR = D / 8;                // 16-byte chunks per row
+  static constexpr int RPB = 256 / ROWB;           // rows per 256-byte sweep of the banks
+  static constexpr int ELEMS = BN * D;             // one tile of K or V
+  static constexpr int NWAVE = NT / 64;
+  static constexpr int DMA = BN * ROWB / 1024 / NWAVE;  // 1 KB global->LDS copies per wave
+  static_assert(BN * ROWB % (1024 * NWAVE) == 0, "tile copy must divide evenly over the waves");
+  static_assert(SPR >= 8, "swizzles assume at least 8 chunks per row");
+  // Physical chunk of logical chunk c of row `key`. K: 16 lanes read one logical chunk of 16
+  // consecutive keys. V: a transposed read covers 4 consecutive keys x 4 consecutive chunks.
+  static __host__ __device__ constexpr int k_swz(int key) { return (key / RPB) & (SPR - 1); }
+  static __host__ __device__ constexpr int v_swz(int key) { return (4 * ((key / RPB) & 3)) & (SPR - 1); }
 };
 
 struct OutBf16 {
@@ -77,26 +91,32 @@ struct OutF32 {
   }
 };
 
-__device__ inline float xor32(float x) { return __shfl_xor(x, 32, 64); }
-
-// Pack bf16 number `e` (0..7) of four 8-element rows into 4 consecutive bf16 (8 bytes).
-__device__ inline u32x2 pick4(const u32x4 (&r)[4], int e) {
-  const int w = e >> 1;
-  u32x2 out;
-  if (e & 1) {
-    out[0] = (r[0][w] >> 16) | (r[1][w] & 0xffff0000u);
-    out[1] = (r[2][w] >> 16) | (r[3][w] & 0xffff0000u);
-  } else {
-    out[0] = (r[0][w] & 0xffffu) | (r[1][w] << 16);
-    out[1] = (r[2][w] & 0xffffu) | (r[3][w] << 16);
-  }
-  return out;
+// Partner lane l^32 combined with the own value: v_permlane32_swap hands every lane both its
+// own value and its partner's (in one order or the other), so max/sum of the pair is exact.
+__device__ inline float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+__device__ inline s16x4 read_tr(const __bf16* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p));
+}
+
+// Position of the (step, tile) sequence a workgroup walks: step s of the ring, tile t of
+// that step's share, nt tiles visible in the step, the first nf of them fully visible.
+struct Cursor {
+  int s, t, nt, nf;
+};
+
 template <int D, class Out>
-__global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(const AttnArgs a) {
+__global__ __launch_bounds__(NT, RA_ATTN_WAVES_PER_SIMD) void attn_bf16_kernel(const AttnArgs a) {
   using C = Cfg<D>;
-  __shared__ __attribute__((aligned(16))) __bf16 smem[2 * C::STAGE];
+  __shared__ __attribute__((aligned(1024))) __bf16 k_lds[2][C::ELEMS];
+  __shared__ __attribute__((aligned(1024))) __bf16 v_lds[2][C::ELEMS];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -121,28 +141,18 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(const AttnArgs a) {
   // ---- Q rows of this wave as B operands (k = head dim), resident for the whole kernel.
   bf16x8 qreg[D / 16];
   {
-    const __bf16* qp = (const __bf16*)a.q + ((int64_t)b * a.Sq + qrow) * rs + (int64_t)h * D + hh * 8;
+    const int qr = qvalid ? qrow : a.Sq - 1;
+    const __bf16* qp = (const __bf16*)a.q + ((int64_t)b * a.Sq + qr) * rs + (int64_t)h * D + hh * 8;
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
-      if (qvalid) {
-        qreg[ks] = *(const bf16x8*)(qp + ks * 16);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) qreg[ks][e] = (__bf16)0.0f;
-      }
-    }
+    for (int ks = 0; ks < D / 16; ++ks) qreg[ks] = *(const bf16x8*)(qp + ks * 16);
   }
 
   // ---- positions of the workgroup's, the wave's and this lane's query rows.
-  int64_t wg_qmin = 0, wg_qmax = 0, w_qmin = 0, w_qmax = 0, my_qpos = -1;
+  int64_t wg_qmin = 0, wg_qmax = 0, w_qmin = 0, my_qpos = -1;
   if (a.causal) {
-    const int last = min(q0 + BM, a.Sq) - 1;
     wg_qmin = pos_of(a.qpos, q0);
-    wg_qmax = pos_of(a.qpos, last);
-    if (wave_live) {
-      w_qmin = pos_of(a.qpos, w0);
-      w_qmax = pos_of(a.qpos, min(w0 + 32, a.Sq) - 1);
-    }
+    wg_qmax = pos_of(a.qpos, min(q0 + BM, a.Sq) - 1);
+    if (wave_live) w_qmin = pos_of(a.qpos, w0);
     if (qvalid) my_qpos = pos_of(a.qpos, qrow);
   }
 
@@ -171,176 +181,213 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(const AttnArgs a) {
   }
 
   // ---- the (step, tile) sequence this workgroup visits.
-  auto share_rule = [&](int s) { return make_pos(a.kv_assign, a.kv_world, a.kv_rank[s], a.kv_len); };
-  auto tiles_of = [&](int s) -> int {
-    if (!a.causal) return (a.Sk + BN - 1) / BN;
-    const int64_t n = clamp64(count_le(share_rule(s), wg_qmax), 0, a.Sk);
-    return (int)((n + BN - 1) / BN);
-  };
-
-  int s = 0, t = 0;
-  int nts = a.nsteps > 0 ? tiles_of(0) : 0;
-  bool have = a.nsteps > 0;
-  while (have && nts == 0) {
-    if (++s >= a.nsteps) { have = false; break; }
-    nts = tiles_of(s);
-  }
-
-  u32x4 pk[C::K_PER_T];
-  u32x4 pv[C::V_PER_T][4];
-
-  auto fetch = [&](int fs, int ft) {
-    const __bf16* kb = (const __bf16*)a.k[fs] + (int64_t)b * a.Sk * rs + (int64_t)h * D;
-    const __bf16* vb = (const __bf16*)a.v[fs] + (int64_t)b * a.Sk * rs + (int64_t)h * D;
-    const int key0 = ft * BN;
-#pragma unroll
-    for (int i = 0; i < C::K_PER_T; ++i) {
-      const int u = tid + i * NT;
-      const int key = key0 + u / C::KCH;
-      const int ch = u % C::KCH;
-      pk[i] = (u32x4){0u, 0u, 0u, 0u};
-      if (u < C::K_UNITS && key < a.Sk) pk[i] = *(const u32x4*)(kb + key * rs + ch * 8);
+  const Pos kv_rule = make_pos(a.kv_assign, a.kv_world, 0, a.kv_len);  // rank set per step
+  auto step_tiles = [&](int s, int& nt, int& nf) {
+    if (!a.causal) {
+      nt = (a.Sk + BN - 1) / BN;
+      nf = a.Sk / BN;
+      return;
     }
-#pragma unroll
-    for (int i = 0; i < C::V_PER_T; ++i) {
-      const int u = tid + i * NT;
-      const int g = u / C::KCH;
-      const int ch = u % C::KCH;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int key = key0 + g * 4 + e;
-        pv[i][e] = (u32x4){0u, 0u, 0u, 0u};
-        if (u < C::V_UNITS && key < a.Sk) pv[i][e] = *(const u32x4*)(vb + key * rs + ch * 8);
+    Pos kp = kv_rule;
+    kp.rank = a.kv_rank[s];
+    const int64_t cmax = clamp64(count_le(kp, wg_qmax), 0, a.Sk);
+    const int64_t cmin = clamp64(count_le(kp, wg_qmin), 0, a.Sk);
+    nt = (int)((cmax + BN - 1) / BN);
+    nf = (int)(cmin / BN);
+  };
+  // Move to the next tile; at the end the cursor stays on the last tile (a harmless dummy).
+  auto advance = [&](Cursor& c) {
+    if (c.t + 1 < c.nt) {
+      ++c.t;
+      return;
+    }
+    for (int s = c.s + 1; s < a.nsteps; ++s) {
+      int nt, nf;
+      step_tiles(s, nt, nf);
+      if (nt > 0) {
+        c.s = s;
+        c.t = 0;
+        c.nt = nt;
+        c.nf = nf;
+        return;
       }
     }
   };
 
-  auto stash = [&](int stage) {
-    __bf16* ks_ = smem + stage * C::STAGE;
-    __bf16* vt_ = ks_ + C::K_ELEMS;
-#pragma unroll
-    for (int i = 0; i < C::K_PER_T; ++i) {
-      const int u = tid + i * NT;
-      if (u < C::K_UNITS) *(u32x4*)(ks_ + (u / C::KCH) * C::KS + (u % C::KCH) * 8) = pk[i];
+  int total = 0;
+  Cursor cur = {0, 0, 0, 0};
+  bool found = false;
+  for (int s = 0; s < a.nsteps; ++s) {
+    int nt, nf;
+    step_tiles(s, nt, nf);
+    if (nt > 0 && !found) {
+      cur = {s, 0, nt, nf};
+      found = true;
     }
-#pragma unroll
-    for (int i = 0; i < C::V_PER_T; ++i) {
-      const int u = tid + i * NT;
-      if (u < C::V_UNITS) {
-        const int g = u / C::KCH;  // keys 4g .. 4g+3 of the tile
-        const int ch = u % C::KCH;
-        // key index bits: [.. g/4 | bit3 bit2 | bit1 bit0]; stored with bits 2,3 swapped.
-        const int col = (g >> 2) * 16 + 4 * (((g & 1) << 1) | ((g >> 1) & 1));
-#pragma unroll
-        for (int e = 0; e < 8; ++e) *(u32x2*)(vt_ + (ch * 8 + e) * C::VS + col) = pick4(pv[i], e);
-      }
-    }
-  };
-
-  if (have) {
-    fetch(s, t);
-    stash(0);
+    total += nt;
   }
-  __syncthreads();
 
-  int stage = 0;
-  while (have) {
-    // next (step, tile)
-    int ns = s, nt = t + 1, nnts = nts;
-    bool nhave = true;
-    while (nt >= nnts) {
-      if (++ns >= a.nsteps) { nhave = false; break; }
-      nt = 0;
-      nnts = tiles_of(ns);
-    }
-    if (nhave) fetch(ns, nt);
+  if (total > 0) {
+    // Copy one tile (K or V of cursor c) from HBM into an LDS tile with the swizzle `swz`.
+    // Wave w moves rows [w*BN/NWAVE, (w+1)*BN/NWAVE); the ragged tail re-reads a valid row.
+    auto dma = [&](const Cursor& c, const void* const* base, __bf16* tile, auto swz) {
+      const __bf16* p = (const __bf16*)base[c.s] + ((int64_t)b * a.Sk + c.t * BN) * rs + (int64_t)h * D;
+      const int lim = a.Sk - 1 - c.t * BN;
+#pragma unroll
+      for (int i = 0; i < C::DMA; ++i) {
+        const int slot = (wave * C::DMA + i) * 64 + lane;  // 16-byte slot of the LDS tile
+        const int row = slot / C::SPR;
+        const int chunk = (slot % C::SPR) ^ swz(row);
+        const __bf16* src = p + (int64_t)min(row, lim) * rs + chunk * 8;
+        __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(tile + (wave * C::DMA + i) * 512),
+                                         16, 0, 0);
+      }
+    };
+    auto k_swz = [](int key) { return C::k_swz(key); };
+    auto v_swz = [](int key) { return C::v_swz(key); };
+    // Lane-constant byte offsets of the swizzled reads (the XOR depends only on the lane).
+    int kofs[D / 16];
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) kofs[ks] = l32 * C::ROWB + (((2 * ks + hh) ^ C::k_swz(l32)) * 16);
+    const int g16 = lane >> 4, jj = lane & 15;
+    const int vrow = 4 * (g16 >> 1) + (jj >> 2);  // key of this lane's transposed-read address
+    int vofs[D / 32];
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+      vofs[db] = vrow * C::ROWB + (((4 * db + 2 * (g16 & 1) + ((jj & 3) >> 1)) ^ C::v_swz(vrow)) * 16) + (jj & 1) * 8;
 
-    // classify this tile for the wave
-    const Pos kvp = share_rule(s);
-    const int key0 = t * BN;
-    const int klast = min(key0 + BN, a.Sk) - 1;
-    bool skip = !wave_live;
-    bool masked = key0 + BN > a.Sk;
-    if (a.causal && wave_live) {
-      const int64_t kmin = pos_of(kvp, key0);
-      const int64_t kmax = pos_of(kvp, klast);
-      skip = w_qmax < kmin;
-      masked = masked || (w_qmin < kmax);
-    }
-
-    if (!skip) {
-      const __bf16* ks_ = smem + stage * C::STAGE;
-      const __bf16* vt_ = ks_ + C::K_ELEMS;
-      f32x16 sacc[BN / 32];
+    auto qk = [&](const __bf16* kt, f32x16 (&s)[BN / 32]) {
+      const char* kb8 = (const char*)kt;
 #pragma unroll
       for (int kb = 0; kb < BN / 32; ++kb) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
+        for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
 #pragma unroll
         for (int ks = 0; ks < D / 16; ++ks) {
-          const bf16x8 ka = *(const bf16x8*)(ks_ + (kb * 32 + l32) * C::KS + ks * 16 + hh * 8);
-          sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qreg[ks], sacc[kb], 0, 0, 0);
+          const bf16x8 ka = *(const bf16x8*)(kb8 + kofs[ks] + kb * 32 * C::ROWB);
+          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qreg[ks], s[kb], 0, 0, 0);
         }
       }
+    };
+
+    // Phase A of folding tile `c` (scores in s): causal/ragged mask where the tile needs
+    // one, the tile's row max and, when it exceeds the running max by more than kLazy, the
+    // rescale of O and l. Returns the reference value the tile's weights are taken against.
+    auto prepare = [&](const Cursor& c, f32x16 (&s)[BN / 32]) -> float {
+      const int key0 = c.t * BN;
+      bool masked = key0 + BN > a.Sk;
+      Pos kvp = kv_rule;
+      kvp.rank = a.kv_rank[c.s];
+      if (a.causal) masked = masked || (c.t >= c.nf && w_qmin < pos_of(kvp, min(key0 + BN, a.Sk) - 1));
       if (masked) {
 #pragma unroll
         for (int kb = 0; kb < BN / 32; ++kb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int key = key0 + kb * 32 + (r >> 2) * 8 + hh * 4 + (r & 3);
-            bool vis = key < a.Sk;
-            if (a.causal) vis = vis && visible(my_qpos, pos_of(kvp, key));
-            if (!vis) sacc[kb][r] = -INFINITY;
+            const bool vis = (key < a.Sk) & (!a.causal | visible(my_qpos, pos_of(kvp, key)));
+            s[kb][r] = vis ? s[kb][r] : -INFINITY;
           }
       }
-      // online softmax update (log2 domain)
-      float mt = -INFINITY;
+      float mt = s[0][0];
 #pragma unroll
       for (int kb = 0; kb < BN / 32; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sacc[kb][r]);
-      mt = fmaxf(mt, xor32(mt));
-      const float m_new = fmaxf(m_run, mt * sl2);
-      const float base = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - base);
-      m_run = m_new;
-      l_run *= alpha;
+        for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[kb][r]);
+      const float mc = pair_max(mt) * sl2;
+      const bool upd = mc > m_run + kLazy;
+      if (__any(upd)) {
+        // lanes that keep their reference value (possibly -inf: no visible key yet) keep O
+        const float alpha = upd ? __builtin_amdgcn_exp2f(m_run - mc) : 1.f;
+        m_run = upd ? mc : m_run;
+        l_run *= alpha;
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db)
+        for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+          for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+      }
+      return m_run == -INFINITY ? 0.f : m_run;
+    };
 
-      bf16x8 pb[BN / 32][2];
+    // Phase B, one branch-free block: the weights of the current tile (exp2), O^T += V^T P^T
+    // for it, and the next tile's S^T = K Q^T, in four chunks of 16 keys so that the MFMAs of
+    // both products are issued between the VALU work of the softmax.
+    auto fold_and_score = [&](f32x16 (&sc)[BN / 32], float base, const __bf16* vt, f32x16 (&sn)[BN / 32],
+                              const __bf16* kt) {
 #pragma unroll
       for (int kb = 0; kb < BN / 32; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(sacc[kb][r], sl2, -base));
+        for (int r = 0; r < 16; ++r) sn[kb][r] = 0.f;
+      const char* vt8 = (const char*)vt;
+      const char* kt8 = (const char*)kt;
+#pragma unroll
+      for (int ch = 0; ch < 2 * (BN / 32); ++ch) {
+        const int kb = ch >> 1, j = ch & 1;
+        bf16x8 pb;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float p = __builtin_amdgcn_exp2f(fmaf(sc[kb][j * 8 + e], sl2, -base));
           l_run += p;
-          pb[kb][r >> 3][r & 7] = (__bf16)p;
+          pb[e] = (__bf16)p;
         }
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db)
+        for (int db = 0; db < D / 32; ++db) {
+          const char* vp = vt8 + vofs[db] + (kb * 32 + j * 16) * C::ROWB;
+          const s16x4 lo = read_tr((const __bf16*)vp);
+          const s16x4 hi = read_tr((const __bf16*)(vp + 8 * C::ROWB));
+          const s16x8 w = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w), pb, oacc[db], 0, 0, 0);
+        }
+        // next tile's scores: key block kb, head-dim steps 8j/2 .. 8j/2+3 of its chain
+        constexpr int KSTEPS = D / 16;
 #pragma unroll
-        for (int kb = 0; kb < BN / 32; ++kb)
-#pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            const bf16x8 va = *(const bf16x8*)(vt_ + (db * 32 + l32) * C::VS + kb * 32 + j * 16 + hh * 8);
-            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[kb][j], oacc[db], 0, 0, 0);
-          }
-    }
+        for (int q = 0; q < KSTEPS / 2; ++q) {
+          const int ks = j * (KSTEPS / 2) + q;
+          const bf16x8 ka = *(const bf16x8*)(kt8 + kofs[ks] + kb * 32 * C::ROWB);
+          sn[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qreg[ks], sn[kb], 0, 0, 0);
+        }
+      }
+    };
 
-    if (nhave) stash(stage ^ 1);
+    // Prologue: K and V of tile 0 and K of tile 1 resident.
+    Cursor nx = cur;
+    advance(nx);
+    Cursor k2 = nx;
+    advance(k2);
+    dma(cur, a.k, k_lds[0], k_swz);
+    dma(cur, a.v, v_lds[0], v_swz);
+    dma(nx, a.k, k_lds[1], k_swz);
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's copies have landed in LDS
     __syncthreads();
-    stage ^= 1;
-    s = ns;
-    t = nt;
-    nts = nnts;
-    have = nhave;
+
+    f32x16 s0[BN / 32], s1[BN / 32];
+    if (wave_live) qk(k_lds[0], s0);
+    __syncthreads();  // every wave has read K(0) before iteration 0 copies K(2) over it
+    // Iteration j: LDS holds K(j+1) in k_lds[(j+1)&1] and V(j) in v_lds[j&1]; registers hold
+    // the scores of tile j. It loads K(j+2) and V(j+1), computes the scores of tile j+1,
+    // folds tile j in, and writes K(j+2) over K(j) and V(j+1) over V(j-1).
+    auto iteration = [&](int sl, f32x16 (&sc)[BN / 32], f32x16 (&sn)[BN / 32]) {
+      dma(k2, a.k, k_lds[sl], k_swz);
+      dma(nx, a.v, v_lds[sl ^ 1], v_swz);
+      if (wave_live) {
+        const float base = prepare(cur, sc);
+        fold_and_score(sc, base, v_lds[sl], sn, k_lds[sl ^ 1]);
+      }
+      __builtin_amdgcn_s_waitcnt(0);  // this wave's copies have landed in LDS
+      __syncthreads();
+      cur = nx;
+      nx = k2;
+      advance(k2);
+    };
+    for (int j = 0; j < total; j += 2) {
+      iteration(0, s0, s1);
+      if (j + 1 >= total) break;
+      iteration(1, s1, s0);
+    }
   }
 
   // ---- epilogue
-  const float l_tot = l_run + xor32(l_run);
+  const float l_tot = pair_sum(l_run);
   if (!qvalid) return;
   if (a.store_final) {
     const bool any = l_tot > 0.f;
