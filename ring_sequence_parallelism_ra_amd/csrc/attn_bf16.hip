@@ -119,7 +119,7 @@ __global__ __launch_bounds__(NT, RA_ATTN_WAVES_PER_SIMD) void attn_bf16_kernel(c
   __shared__ __attribute__((aligned(1024))) __bf16 v_lds[2][C::ELEMS];
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keep in SGPRs
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int hh = lane >> 5;
@@ -148,7 +148,7 @@ __global__ __launch_bounds__(NT, RA_ATTN_WAVES_PER_SIMD) void attn_bf16_kernel(c
   }
 
   // ---- positions of the workgroup's, the wave's and this lane's query rows.
-  int64_t wg_qmin = 0, wg_qmax = 0, w_qmin = 0, my_qpos = -1;
+  int32_t wg_qmin = 0, wg_qmax = 0, w_qmin = 0, my_qpos = -1;
   if (a.causal) {
     wg_qmin = pos_of(a.qpos, q0);
     wg_qmax = pos_of(a.qpos, min(q0 + BM, a.Sq) - 1);
@@ -165,16 +165,16 @@ __global__ __launch_bounds__(NT, RA_ATTN_WAVES_PER_SIMD) void attn_bf16_kernel(c
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
 
-  const int64_t state_row = ((int64_t)b * a.H + h) * a.Sq + qrow;          // [B, H, S]
-  const int64_t out_row = (((int64_t)b * a.Sq + qrow) * a.H + h) * D;       // [B, S, H, D]
+  auto state_row = [&]() { return ((int64_t)b * a.H + h) * a.Sq + qrow; };    // [B, H, S]
+  auto out_row = [&]() { return (((int64_t)b * a.Sq + qrow) * a.H + h) * D; };  // [B, S, H, D]
   if (a.load_state && qvalid) {
-    m_run = (float)a.ws_m[state_row];  // stored from this kernel's own fp32 values: exact
-    l_run = hh == 0 ? (float)a.ws_l[state_row] : 0.f;
+    m_run = (float)a.ws_m[state_row()];  // stored from this kernel's own fp32 values: exact
+    l_run = hh == 0 ? (float)a.ws_l[state_row()] : 0.f;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        f32x4 x = *(const f32x4*)(a.ws_o + out_row + db * 32 + g * 8 + hh * 4);
+        f32x4 x = *(const f32x4*)(a.ws_o + out_row() + db * 32 + g * 8 + hh * 4);
 #pragma unroll
         for (int e = 0; e < 4; ++e) oacc[db][g * 4 + e] = x[e];
       }
@@ -190,10 +190,10 @@ __global__ __launch_bounds__(NT, RA_ATTN_WAVES_PER_SIMD) void attn_bf16_kernel(c
     }
     Pos kp = kv_rule;
     kp.rank = a.kv_rank[s];
-    const int64_t cmax = clamp64(count_le(kp, wg_qmax), 0, a.Sk);
-    const int64_t cmin = clamp64(count_le(kp, wg_qmin), 0, a.Sk);
-    nt = (int)((cmax + BN - 1) / BN);
-    nf = (int)(cmin / BN);
+    const int32_t cmax = clamp32(count_le(kp, wg_qmax), 0, a.Sk);
+    const int32_t cmin = clamp32(count_le(kp, wg_qmin), 0, a.Sk);
+    nt = (cmax + BN - 1) / BN;
+    nf = cmin / BN;
   };
   // Move to the next tile; at the end the cursor stays on the last tile (a harmless dummy).
   auto advance = [&](Cursor& c) {
@@ -231,15 +231,16 @@ __global__ __launch_bounds__(NT, RA_ATTN_WAVES_PER_SIMD) void attn_bf16_kernel(c
     // Copy one tile (K or V of cursor c) from HBM into an LDS tile with the swizzle `swz`.
     // Wave w moves rows [w*BN/NWAVE, (w+1)*BN/NWAVE); the ragged tail re-reads a valid row.
     auto dma = [&](const Cursor& c, const void* const* base, __bf16* tile, auto swz) {
-      const __bf16* p = (const __bf16*)base[c.s] + ((int64_t)b * a.Sk + c.t * BN) * rs + (int64_t)h * D;
+      const char* p = (const char*)base[c.s] + (((int64_t)b * a.Sk + c.t * BN) * rs + (int64_t)h * D) * 2;
       const int lim = a.Sk - 1 - c.t * BN;
+      const uint32_t rowb = (uint32_t)rs * 2;
 #pragma unroll
       for (int i = 0; i < C::DMA; ++i) {
         const int slot = (wave * C::DMA + i) * 64 + lane;  // 16-byte slot of the LDS tile
         const int row = slot / C::SPR;
         const int chunk = (slot % C::SPR) ^ swz(row);
-        const __bf16* src = p + (int64_t)min(row, lim) * rs + chunk * 8;
-        __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(tile + (wave * C::DMA + i) * 512),
+        const uint32_t off = (uint32_t)min(row, lim) * rowb + (uint32_t)chunk * 16;
+        __builtin_amdgcn_global_load_lds(p + off, (__attribute__((address_space(3))) void*)(tile + (wave * C::DMA + i) * 512),
                                          16, 0, 0);
       }
     };
@@ -280,13 +281,15 @@ __global__ __launch_bounds__(NT, RA_ATTN_WAVES_PER_SIMD) void attn_bf16_kernel(c
       kvp.rank = a.kv_rank[c.s];
       if (a.causal) masked = masked || (c.t >= c.nf && w_qmin < pos_of(kvp, min(key0 + BN, a.Sk) - 1));
       if (masked) {
+        // The keys this lane's query sees form a prefix of the share: mask from its length.
+        const int32_t nvis = a.causal ? clamp32(count_le(kvp, my_qpos), 0, a.Sk) : a.Sk;
+        const int lim = nvis - key0 - hh * 4;  // compared with the lane's key offsets
 #pragma unroll
         for (int kb = 0; kb < BN / 32; ++kb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int key = key0 + kb * 32 + (r >> 2) * 8 + hh * 4 + (r & 3);
-            const bool vis = (key < a.Sk) & (!a.causal | visible(my_qpos, pos_of(kvp, key)));
-            s[kb][r] = vis ? s[kb][r] : -INFINITY;
+            const int off = kb * 32 + (r >> 2) * 8 + (r & 3);
+            s[kb][r] = off < lim ? s[kb][r] : -INFINITY;
           }
       }
       float mt = s[0][0];
@@ -399,9 +402,9 @@ __global__ __launch_bounds__(NT, RA_ATTN_WAVES_PER_SIMD) void attn_bf16_kernel(c
         f32x4 x;
 #pragma unroll
         for (int e = 0; e < 4; ++e) x[e] = oacc[db][g * 4 + e] * inv;
-        Out::store4(a.o, out_row + db * 32 + g * 8 + hh * 4, x);
+        Out::store4(a.o, out_row() + db * 32 + g * 8 + hh * 4, x);
       }
-    if (hh == 0) a.lse[state_row] = any ? (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
+    if (hh == 0) a.lse[state_row()] = any ? (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
   } else {
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
@@ -410,11 +413,11 @@ __global__ __launch_bounds__(NT, RA_ATTN_WAVES_PER_SIMD) void attn_bf16_kernel(c
         f32x4 x;
 #pragma unroll
         for (int e = 0; e < 4; ++e) x[e] = oacc[db][g * 4 + e];
-        *(f32x4*)(a.ws_o + out_row + db * 32 + g * 8 + hh * 4) = x;
+        *(f32x4*)(a.ws_o + out_row() + db * 32 + g * 8 + hh * 4) = x;
       }
     if (hh == 0) {
-      a.ws_m[state_row] = m_run;
-      a.ws_l[state_row] = l_tot;
+      a.ws_m[state_row()] = m_run;
+      a.ws_l[state_row()] = l_tot;
     }
   }
 }

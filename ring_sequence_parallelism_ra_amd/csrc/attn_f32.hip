@@ -39,7 +39,7 @@ __global__ __launch_bounds__(BM) void attn_f32_kernel(const AttnArgs a) {
   float* q = qs_ + lane * (D + 1);
   for (int d = 0; d < D; ++d) q[d] = qvalid ? qp[d] : 0.f;
 
-  int64_t wg_qmax = 0, my_qpos = -1;
+  int32_t wg_qmax = 0, my_qpos = -1;
   if (a.causal) {
     wg_qmax = pos_of(a.qpos, min(q0 + BM, a.Sq) - 1);
     if (qvalid) my_qpos = pos_of(a.qpos, qrow);
@@ -61,8 +61,8 @@ __global__ __launch_bounds__(BM) void attn_f32_kernel(const AttnArgs a) {
 
   for (int s = 0; s < a.nsteps; ++s) {
     const Pos kvp = make_pos(a.kv_assign, a.kv_world, a.kv_rank[s], a.kv_len);
-    int64_t nvis = a.Sk;
-    if (a.causal) nvis = clamp64(count_le(kvp, wg_qmax), 0, a.Sk);
+    int32_t nvis = a.Sk;
+    if (a.causal) nvis = clamp32(count_le(kvp, wg_qmax), 0, a.Sk);
     const float* kb = (const float*)a.k[s] + (int64_t)b * a.Sk * rs + (int64_t)h * D;
     const float* vb = (const float*)a.v[s] + (int64_t)b * a.Sk * rs + (int64_t)h * D;
     for (int key0 = 0; key0 < nvis; key0 += BN) {

@@ -147,14 +147,14 @@ __global__ __launch_bounds__(256) void permute_kernel(const char* __restrict__ i
 
 __global__ void positions_kernel(Pos p, int64_t n, int64_t* out) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) out[i] = pos_of(p, i);
+  if (i < n) out[i] = pos_of(p, (int32_t)i);
 }
 
 __global__ void mask_kernel(Pos q, Pos kv, int64_t Sq, int64_t Sk, uint8_t* out) {
   const int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (u >= Sq * Sk) return;
   const int64_t i = u / Sk, j = u % Sk;
-  out[u] = visible(pos_of(q, i), pos_of(kv, j)) ? 1 : 0;
+  out[u] = visible(pos_of(q, (int32_t)i), pos_of(kv, (int32_t)j)) ? 1 : 0;
 }
 
 }  // namespace

@@ -39,6 +39,8 @@ int check_shard(const ra_shard* sh, int64_t S, const char* what) {
   if (sh->rank < 0 || sh->rank >= sh->world)
     return fail(RA_ERR_INVALID_ARG, "%s: rank %d not in [0, %d)", what, sh->rank, sh->world);
   if (sh->global_len < 0) return fail(RA_ERR_INVALID_ARG, "%s: negative global_len", what);
+  if (sh->global_len >= ((int64_t)1 << 31))
+    return fail(RA_ERR_UNSUPPORTED, "%s: global_len %lld >= 2^31", what, (long long)sh->global_len);
   const int64_t parts = sh->assign == RA_ZIGZAG ? 2 * (int64_t)sh->world : sh->world;
   if (sh->global_len % parts)
     return fail(RA_ERR_SHAPE, "%s: global_len %lld not divisible by %lld", what,
@@ -151,6 +153,7 @@ int ra_ring_share(const void* q, const void* const* k_shares, const void* const*
                 start_step + num_steps, N);
   if (isnan(scale) || isinf(scale)) return fail(RA_ERR_INVALID_ARG, "scale is not finite");
   const int64_t L = (int64_t)N * S_loc;
+  if (L >= ((int64_t)1 << 31)) return fail(RA_ERR_UNSUPPORTED, "global length N*S_loc = %lld >= 2^31", (long long)L);
   if (causal && assign == RA_ZIGZAG && S_loc % 2)
     return fail(RA_ERR_SHAPE, "zigzag needs L %% 2N == 0 (S_loc=%lld is odd)", (long long)S_loc);
   const bool load_state = start_step > 0;
@@ -267,12 +270,12 @@ int ra_share_work(const ra_shard* q_sh, const ra_shard* kv_sh, int64_t Sq, int64
   }
   const ra::Pos qp = to_pos(*q_sh), kp = to_pos(*kv_sh);
   int64_t pairs = 0;
-  for (int64_t i = 0; i < Sq; ++i) pairs += ra::clamp64(ra::count_le(kp, ra::pos_of(qp, i)), 0, Sk);
+  for (int64_t i = 0; i < Sq; ++i) pairs += ra::clamp64(ra::count_le(kp, ra::pos_of(qp, (int32_t)i)), 0, Sk);
   int64_t full = 0, partial = 0, skip = 0;
   for (int64_t t = 0; t < n_qt; ++t) {
     const int64_t r0 = t * block_m, r1 = (r0 + block_m < Sq ? r0 + block_m : Sq) - 1;
-    const int64_t cmin = ra::clamp64(ra::count_le(kp, ra::pos_of(qp, r0)), 0, Sk);
-    const int64_t cmax = ra::clamp64(ra::count_le(kp, ra::pos_of(qp, r1)), 0, Sk);
+    const int64_t cmin = ra::clamp64(ra::count_le(kp, ra::pos_of(qp, (int32_t)r0)), 0, Sk);
+    const int64_t cmax = ra::clamp64(ra::count_le(kp, ra::pos_of(qp, (int32_t)r1)), 0, Sk);
     // Tiles made only of keys visible to the tile's first (smallest-position) row are full.
     const int64_t nfull = cmin / block_n + ((cmin == Sk && Sk % block_n) ? 1 : 0);
     const int64_t active = (cmax + block_n - 1) / block_n;

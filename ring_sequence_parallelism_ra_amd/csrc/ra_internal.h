@@ -13,13 +13,14 @@
 
 namespace ra {
 
-// Position rule of one share: local row i -> global token position.
+// Position rule of one share: local row i -> global token position. Global lengths are
+// validated to stay below 2^31, so positions and counts fit 32-bit integers.
 struct Pos {
   int32_t assign;  // ra_assign
   int32_t world;
   int32_t rank;
-  int64_t share;   // rows per share, L / N
-  int64_t chunk;   // zigzag chunk length, L / (2N) (unused otherwise)
+  int32_t share;   // rows per share, L / N
+  int32_t chunk;   // zigzag chunk length, L / (2N) (unused otherwise)
 };
 
 __host__ __device__ inline Pos make_pos(int assign, int world, int rank, int64_t len) {
@@ -27,16 +28,20 @@ __host__ __device__ inline Pos make_pos(int assign, int world, int rank, int64_t
   p.assign = assign;
   p.world = world;
   p.rank = rank;
-  p.share = len / world;
-  p.chunk = len / (2 * (int64_t)world);
+  p.share = (int32_t)(len / world);
+  p.chunk = (int32_t)(len / (2 * (int64_t)world));
   return p;
 }
 
-__host__ __device__ inline int64_t pos_of(const Pos& p, int64_t i) {
+__host__ __device__ inline int32_t pos_of(const Pos& p, int32_t i) {
   if (p.assign == RA_STRIPED) return i * p.world + p.rank;
   if (p.assign == RA_ZIGZAG)
-    return i < p.chunk ? p.rank * p.chunk + i : (2 * (int64_t)p.world - 1 - p.rank) * p.chunk + (i - p.chunk);
+    return i < p.chunk ? p.rank * p.chunk + i : (2 * p.world - 1 - p.rank) * p.chunk + (i - p.chunk);
   return p.rank * p.share + i;  // RA_CONTIGUOUS
+}
+
+__host__ __device__ inline int32_t clamp32(int32_t x, int32_t lo, int32_t hi) {
+  return x < lo ? lo : (x > hi ? hi : x);
 }
 
 __host__ __device__ inline int64_t clamp64(int64_t x, int64_t lo, int64_t hi) {
@@ -45,21 +50,21 @@ __host__ __device__ inline int64_t clamp64(int64_t x, int64_t lo, int64_t hi) {
 
 // Number of local rows whose global position is <= x. Positions increase with the local
 // row index under all three assignments, so these rows are a prefix of the share.
-__host__ __device__ inline int64_t count_le(const Pos& p, int64_t x) {
+__host__ __device__ inline int32_t count_le(const Pos& p, int32_t x) {
   if (p.assign == RA_STRIPED) {
     if (x < p.rank) return 0;
-    return clamp64((x - p.rank) / p.world + 1, 0, p.share);
+    return clamp32((x - p.rank) / p.world + 1, 0, p.share);
   }
   if (p.assign == RA_ZIGZAG) {
-    int64_t lo = clamp64(x - p.rank * p.chunk + 1, 0, p.chunk);
-    int64_t hi = clamp64(x - (2 * (int64_t)p.world - 1 - p.rank) * p.chunk + 1, 0, p.chunk);
+    const int32_t lo = clamp32(x - p.rank * p.chunk + 1, 0, p.chunk);
+    const int32_t hi = clamp32(x - (2 * p.world - 1 - p.rank) * p.chunk + 1, 0, p.chunk);
     return lo + hi;
   }
-  return clamp64(x - p.rank * p.share + 1, 0, p.share);
+  return clamp32(x - p.rank * p.share + 1, 0, p.share);
 }
 
 // Causal visibility by global position, diagonal included ([Digest] §3.4 causal matrix).
-__host__ __device__ inline bool visible(int64_t qpos, int64_t kpos) { return kpos <= qpos; }
+__host__ __device__ inline bool visible(int32_t qpos, int32_t kpos) { return kpos <= qpos; }
 
 constexpr int kMaxSteps = RA_MAX_WORLD;
 
