@@ -55,6 +55,9 @@ constexpr int NT = 256;           // threads per workgroup (4 wave64)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kLazy = 8.f;      // max growth (log2 units) absorbed without rescaling O
+#ifndef RA_ATTN_SCHED
+#define RA_ATTN_SCHED 1               // pin the MFMA / VALU / LDS-read interleave of the main block
+#endif
 #ifndef RA_ATTN_WAVES_PER_SIMD
 #define RA_ATTN_WAVES_PER_SIMD 2      // occupancy target: 256 VGPRs per wave at 2, 512 at 1
 #endif
@@ -333,6 +336,8 @@ __global__ __launch_bounds__(NT, RA_ATTN_WAVES_PER_SIMD) void attn_bf16_kernel(c
           l_run += p;
           pb[e] = (__bf16)p;
         }
+        // O^T += V^T P^T for these 16 keys (one MFMA per 32 head-dim rows), alternating with
+        // the next tile's S^T chain for key block kb, head-dim steps j*D/32 .. j*D/32 + D/32-1.
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
           const char* vp = vt8 + vofs[db] + (kb * 32 + j * 16) * C::ROWB;
@@ -340,16 +345,27 @@ __global__ __launch_bounds__(NT, RA_ATTN_WAVES_PER_SIMD) void attn_bf16_kernel(c
           const s16x4 hi = read_tr((const __bf16*)(vp + 8 * C::ROWB));
           const s16x8 w = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
           oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w), pb, oacc[db], 0, 0, 0);
-        }
-        // next tile's scores: key block kb, head-dim steps 8j/2 .. 8j/2+3 of its chain
-        constexpr int KSTEPS = D / 16;
-#pragma unroll
-        for (int q = 0; q < KSTEPS / 2; ++q) {
-          const int ks = j * (KSTEPS / 2) + q;
+          const int ks = j * (D / 32) + db;
           const bf16x8 ka = *(const bf16x8*)(kt8 + kofs[ks] + kb * 32 * C::ROWB);
           sn[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qreg[ks], sn[kb], 0, 0, 0);
         }
       }
+#if RA_ATTN_SCHED
+      // Issue order for the block above: the first chunk's weights, a few operand reads ahead,
+      // then per MFMA a short run of VALU work (next chunk's exp2) and the reads for the MFMAs
+      // two ahead, so LDS latency and the softmax hide under the matrix-core work.
+      __builtin_amdgcn_sched_group_barrier(0x002, 28, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+      for (int i = 0; i < 2 * (BN / 32) * (D / 32); ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+#endif
     };
 
     // Prologue: K and V of tile 0 and K of tile 1 resident.
