@@ -51,12 +51,21 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int BM = kBf16BlockM;   // query rows per workgroup
 constexpr int BN = kBf16BlockN;   // keys per tile
-constexpr int NT = 256;           // threads per workgroup (4 wave64)
+constexpr int NT = 64 * RA_ATTN_WAVES;  // threads per workgroup
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kLazy = 8.f;      // max growth (log2 units) absorbed without rescaling O
 #ifndef RA_ATTN_SCHED
 #define RA_ATTN_SCHED 1               // pin the MFMA / VALU / LDS-read interleave of the main block
+#endif
+#ifndef RA_ATTN_SCHED_VALU
+#define RA_ATTN_SCHED_VALU 3          // VALU ops placed after each MFMA of the main block
+#endif
+#ifndef RA_ATTN_SCHED_AHEAD
+#define RA_ATTN_SCHED_AHEAD 6         // LDS operand reads issued before the first MFMA
+#endif
+#ifndef RA_ATTN_SETPRIO
+#define RA_ATTN_SETPRIO 1             // raise wave priority while issuing the main block
 #endif
 #ifndef RA_ATTN_WAVES_PER_SIMD
 #define RA_ATTN_WAVES_PER_SIMD 2      // occupancy target: 256 VGPRs per wave at 2, 512 at 1
@@ -231,20 +240,37 @@ __global__ __launch_bounds__(NT, RA_ATTN_WAVES_PER_SIMD) void attn_bf16_kernel(c
   }
 
   if (total > 0) {
-    // Copy one tile (K or V of cursor c) from HBM into an LDS tile with the swizzle `swz`.
-    // Wave w moves rows [w*BN/NWAVE, (w+1)*BN/NWAVE); the ragged tail re-reads a valid row.
-    auto dma = [&](const Cursor& c, const void* const* base, __bf16* tile, auto swz) {
+    // Copy one tile (K or V of cursor c) from HBM into an LDS tile. Lane `lane` of copy i of
+    // wave w fills 16-byte slot (w*DMA + i)*64 + lane of the tile, i.e. row slot/SPR and
+    // physical chunk slot%SPR, with logical chunk (slot%SPR) ^ swizzle(row). The per-lane byte
+    // offsets into the tile are fixed, so they are computed once; only a ragged last tile
+    // (rows past Sk re-read a valid row) recomputes them.
+    const uint32_t rowb = (uint32_t)rs * 2;
+    uint32_t koff[C::DMA], voff[C::DMA];
+#pragma unroll
+    for (int i = 0; i < C::DMA; ++i) {
+      const int slot = (wave * C::DMA + i) * 64 + lane;
+      const int row = slot / C::SPR;
+      koff[i] = (uint32_t)row * rowb + (uint32_t)(((slot % C::SPR) ^ C::k_swz(row)) * 16);
+      voff[i] = (uint32_t)row * rowb + (uint32_t)(((slot % C::SPR) ^ C::v_swz(row)) * 16);
+    }
+    auto dma = [&](const Cursor& c, const void* const* base, __bf16* tile, auto swz, const uint32_t* off) {
       const char* p = (const char*)base[c.s] + (((int64_t)b * a.Sk + c.t * BN) * rs + (int64_t)h * D) * 2;
       const int lim = a.Sk - 1 - c.t * BN;
-      const uint32_t rowb = (uint32_t)rs * 2;
+      if (lim >= BN - 1) {
 #pragma unroll
-      for (int i = 0; i < C::DMA; ++i) {
-        const int slot = (wave * C::DMA + i) * 64 + lane;  // 16-byte slot of the LDS tile
-        const int row = slot / C::SPR;
-        const int chunk = (slot % C::SPR) ^ swz(row);
-        const uint32_t off = (uint32_t)min(row, lim) * rowb + (uint32_t)chunk * 16;
-        __builtin_amdgcn_global_load_lds(p + off, (__attribute__((address_space(3))) void*)(tile + (wave * C::DMA + i) * 512),
-                                         16, 0, 0);
+        for (int i = 0; i < C::DMA; ++i)
+          __builtin_amdgcn_global_load_lds(p + off[i], (__attribute__((address_space(3))) void*)(tile + (wave * C::DMA + i) * 512),
+                                           16, 0, 0);
+      } else {
+#pragma unroll
+        for (int i = 0; i < C::DMA; ++i) {
+          const int slot = (wave * C::DMA + i) * 64 + lane;
+          const int row = slot / C::SPR;
+          const uint32_t o = (uint32_t)min(row, lim) * rowb + (uint32_t)(((slot % C::SPR) ^ swz(row)) * 16);
+          __builtin_amdgcn_global_load_lds(p + o, (__attribute__((address_space(3))) void*)(tile + (wave * C::DMA + i) * 512),
+                                           16, 0, 0);
+        }
       }
     };
     auto k_swz = [](int key) { return C::k_swz(key); };
@@ -355,14 +381,14 @@ __global__ __launch_bounds__(NT, RA_ATTN_WAVES_PER_SIMD) void attn_bf16_kernel(c
       // then per MFMA a short run of VALU work (next chunk's exp2) and the reads for the MFMAs
       // two ahead, so LDS latency and the softmax hide under the matrix-core work.
       __builtin_amdgcn_sched_group_barrier(0x002, 28, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, RA_ATTN_SCHED_AHEAD, 0);
 #pragma unroll
       for (int i = 0; i < 2 * (BN / 32) * (D / 32); ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, RA_ATTN_SCHED_VALU, 0);
         __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, RA_ATTN_SCHED_VALU, 0);
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
 #endif
@@ -373,9 +399,9 @@ __global__ __launch_bounds__(NT, RA_ATTN_WAVES_PER_SIMD) void attn_bf16_kernel(c
     advance(nx);
     Cursor k2 = nx;
     advance(k2);
-    dma(cur, a.k, k_lds[0], k_swz);
-    dma(cur, a.v, v_lds[0], v_swz);
-    dma(nx, a.k, k_lds[1], k_swz);
+    dma(cur, a.k, k_lds[0], k_swz, koff);
+    dma(cur, a.v, v_lds[0], v_swz, voff);
+    dma(nx, a.k, k_lds[1], k_swz, koff);
     __builtin_amdgcn_s_waitcnt(0);  // this wave's copies have landed in LDS
     __syncthreads();
 
@@ -386,11 +412,13 @@ __global__ __launch_bounds__(NT, RA_ATTN_WAVES_PER_SIMD) void attn_bf16_kernel(c
     // the scores of tile j. It loads K(j+2) and V(j+1), computes the scores of tile j+1,
     // folds tile j in, and writes K(j+2) over K(j) and V(j+1) over V(j-1).
     auto iteration = [&](int sl, f32x16 (&sc)[BN / 32], f32x16 (&sn)[BN / 32]) {
-      dma(k2, a.k, k_lds[sl], k_swz);
-      dma(nx, a.v, v_lds[sl ^ 1], v_swz);
+      dma(k2, a.k, k_lds[sl], k_swz, koff);
+      dma(nx, a.v, v_lds[sl ^ 1], v_swz, voff);
       if (wave_live) {
         const float base = prepare(cur, sc);
+        if (RA_ATTN_SETPRIO) __builtin_amdgcn_s_setprio(1);
         fold_and_score(sc, base, v_lds[sl], sn, k_lds[sl ^ 1]);
+        if (RA_ATTN_SETPRIO) __builtin_amdgcn_s_setprio(0);
       }
       __builtin_amdgcn_s_waitcnt(0);  // this wave's copies have landed in LDS
       __syncthreads();

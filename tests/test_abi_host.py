@@ -39,6 +39,15 @@ def test_exported_symbols_in_dynamic_table():
         assert name in syms, name
 
 
+def test_no_undefined_library_symbols():
+    # Every symbol the library itself defines must resolve: a kernel whose host launch stub
+    # went missing shows up as an undefined ra:: symbol (the dynamic loader only fails lazily).
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--undefined-only", _lib.LIB_PATH], capture_output=True, text=True).stdout
+    own = [ln for ln in out.splitlines() if "_ZN2ra" in ln or " ra_" in ln]
+    assert not own, own
+
+
 def call_block(**over):
     a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=1, H=2, Sq=64, Sk=64, D=128, ind=1, od=1, causal=0,
              qs=None, ks=None, scale=0.0)
