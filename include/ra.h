@@ -80,6 +80,7 @@ typedef struct {
  * no visible key gets O = 0 and LSE = -inf.
  * in_dtype RA_BF16 runs bf16 MFMA with fp32 accumulation; RA_F32 runs fp32 FMA.
  * D must be 64 or 128. Sq and Sk may be any non-negative size (ragged tails are masked).
+ * Global lengths (q_sh->global_len, kv_sh->global_len) must be below 2^31.
  */
 int ra_block_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                       int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t D,

@@ -10,6 +10,12 @@ from __future__ import annotations
 import ctypes
 import os
 
+# torch ships its own HIP runtime with the same soname (libamdhip64.so.7) as the system one that
+# libra.so links against; the dynamic loader serves the whole process from whichever copy is
+# loaded first. Importing torch first makes the library and torch share torch's runtime (one
+# device context, one set of streams).
+import torch  # noqa: F401
+
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libra.so")
 

@@ -29,11 +29,11 @@
 //    visible keys of a share form a prefix (positions increase along a share), whose length
 //    comes from the position rule. Only tiles straddling the causal boundary or the ragged
 //    tail evaluate the mask. Workgroups are launched heaviest query tile first.
-//  * The softmax runs in the log2 domain (exp2 of scores pre-multiplied by scale*log2 e).
-//    The running max is only raised when a tile's max exceeds it by more than kLazy (so the
-//    weights stay <= 2^kLazy); the O rescale that goes with it is skipped otherwise. The
-//    result does not depend on the reference value subtracted; LSE is converted back to the
-//    natural log at the end.
+//  * The softmax runs in the log2 domain (exp2 of scores pre-multiplied by scale*log2 e), with
+//    the exact running max as reference, so the largest weight so far is exactly 1 in bf16 (this
+//    keeps peaked softmaxes accurate). O and l are rescaled only on tiles where some row's max
+//    grows (a wave-uniform branch, rarely taken once the first tiles have been seen). LSE is
+//    converted back to the natural log at the end.
 #include <math.h>
 
 #include "ra_internal.h"
@@ -54,7 +54,7 @@ constexpr int BN = kBf16BlockN;   // keys per tile
 constexpr int NT = 64 * RA_ATTN_WAVES;  // threads per workgroup
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr float kLazy = 8.f;      // max growth (log2 units) absorbed without rescaling O
+
 #ifndef RA_ATTN_SCHED
 #define RA_ATTN_SCHED 1               // pin the MFMA / VALU / LDS-read interleave of the main block
 #endif
@@ -301,7 +301,7 @@ __global__ __launch_bounds__(NT, RA_ATTN_WAVES_PER_SIMD) void attn_bf16_kernel(c
     };
 
     // Phase A of folding tile `c` (scores in s): causal/ragged mask where the tile needs
-    // one, the tile's row max and, when it exceeds the running max by more than kLazy, the
+    // one, the tile's row max and, where it exceeds the running max, the
     // rescale of O and l. Returns the reference value the tile's weights are taken against.
     auto prepare = [&](const Cursor& c, f32x16 (&s)[BN / 32]) -> float {
       const int key0 = c.t * BN;
@@ -327,7 +327,7 @@ __global__ __launch_bounds__(NT, RA_ATTN_WAVES_PER_SIMD) void attn_bf16_kernel(c
 #pragma unroll
         for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[kb][r]);
       const float mc = pair_max(mt) * sl2;
-      const bool upd = mc > m_run + kLazy;
+      const bool upd = mc > m_run;
       if (__any(upd)) {
         // lanes that keep their reference value (possibly -inf: no visible key yet) keep O
         const float alpha = upd ? __builtin_amdgcn_exp2f(m_run - mc) : 1.f;
@@ -356,12 +356,14 @@ __global__ __launch_bounds__(NT, RA_ATTN_WAVES_PER_SIMD) void attn_bf16_kernel(c
       for (int ch = 0; ch < 2 * (BN / 32); ++ch) {
         const int kb = ch >> 1, j = ch & 1;
         bf16x8 pb;
+        float p[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(sc[kb][j * 8 + e], sl2, -base));
-          l_run += p;
-          pb[e] = (__bf16)p;
+          p[e] = __builtin_amdgcn_exp2f(fmaf(sc[kb][j * 8 + e], sl2, -base));
+          pb[e] = (__bf16)p[e];
         }
+        // the chunk's sums as short trees (no long dependency chains through the block)
+        l_run += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
         // O^T += V^T P^T for these 16 keys (one MFMA per 32 head-dim rows), alternating with
         // the next tile's S^T chain for key block kb, head-dim steps j*D/32 .. j*D/32 + D/32-1.
 #pragma unroll
