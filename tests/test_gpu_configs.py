@@ -11,7 +11,6 @@ from gpu_helpers import check, dev, host, say, shares, oracle_rows, values
 from oracle import attention as OA
 from oracle import permute as OU
 from oracle import positions as OP
-from oracle import ring as OR
 
 pytestmark = pytest.mark.gpu
 
