@@ -36,6 +36,8 @@
 //    converted back to the natural log at the end.
 #include <math.h>
 
+#include <type_traits>
+
 #include "ra_internal.h"
 
 namespace ra {
@@ -127,8 +129,13 @@ struct Cursor {
 template <int D, class Out>
 __global__ __launch_bounds__(NT, RA_ATTN_WAVES_PER_SIMD) void attn_bf16_kernel(const AttnArgs a) {
   using C = Cfg<D>;
-  __shared__ __attribute__((aligned(1024))) __bf16 k_lds[2][C::ELEMS];
-  __shared__ __attribute__((aligned(1024))) __bf16 v_lds[2][C::ELEMS];
+  // The two stages of K and V are four distinct LDS objects: the copies into one stage and the
+  // reads of the other can then be told apart, so no wait for in-flight copies is inserted
+  // before the reads.
+  __shared__ __attribute__((aligned(1024))) __bf16 k_lds0[C::ELEMS];
+  __shared__ __attribute__((aligned(1024))) __bf16 k_lds1[C::ELEMS];
+  __shared__ __attribute__((aligned(1024))) __bf16 v_lds0[C::ELEMS];
+  __shared__ __attribute__((aligned(1024))) __bf16 v_lds1[C::ELEMS];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keep in SGPRs
@@ -382,10 +389,24 @@ __global__ __launch_bounds__(NT, RA_ATTN_WAVES_PER_SIMD) void attn_bf16_kernel(c
       // Issue order for the block above: the first chunk's weights, a few operand reads ahead,
       // then per MFMA a short run of VALU work (next chunk's exp2) and the reads for the MFMAs
       // two ahead, so LDS latency and the softmax hide under the matrix-core work.
+#if RA_ATTN_SCHED == 2
+      // The next tile's score MFMAs need no softmax result: open the block with them, the first
+      // chunk's weights computed in their shadow.
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, RA_ATTN_SCHED_AHEAD, 0);
+#else
       __builtin_amdgcn_sched_group_barrier(0x002, 28, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, RA_ATTN_SCHED_AHEAD, 0);
+#endif
+      constexpr int kPairs = (BN / 32) * (D / 32) * 2 - (RA_ATTN_SCHED == 2 ? 2 : 0);
 #pragma unroll
-      for (int i = 0; i < 2 * (BN / 32) * (D / 32); ++i) {
+      for (int i = 0; i < kPairs; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x002, RA_ATTN_SCHED_VALU, 0);
         __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
@@ -401,25 +422,30 @@ __global__ __launch_bounds__(NT, RA_ATTN_WAVES_PER_SIMD) void attn_bf16_kernel(c
     advance(nx);
     Cursor k2 = nx;
     advance(k2);
-    dma(cur, a.k, k_lds[0], k_swz, koff);
-    dma(cur, a.v, v_lds[0], v_swz, voff);
-    dma(nx, a.k, k_lds[1], k_swz, koff);
+    dma(cur, a.k, k_lds0, k_swz, koff);
+    dma(cur, a.v, v_lds0, v_swz, voff);
+    dma(nx, a.k, k_lds1, k_swz, koff);
     __builtin_amdgcn_s_waitcnt(0);  // this wave's copies have landed in LDS
     __syncthreads();
 
     f32x16 s0[BN / 32], s1[BN / 32];
-    if (wave_live) qk(k_lds[0], s0);
+    if (wave_live) qk(k_lds0, s0);
     __syncthreads();  // every wave has read K(0) before iteration 0 copies K(2) over it
-    // Iteration j: LDS holds K(j+1) in k_lds[(j+1)&1] and V(j) in v_lds[j&1]; registers hold
-    // the scores of tile j. It loads K(j+2) and V(j+1), computes the scores of tile j+1,
-    // folds tile j in, and writes K(j+2) over K(j) and V(j+1) over V(j-1).
-    auto iteration = [&](int sl, f32x16 (&sc)[BN / 32], f32x16 (&sn)[BN / 32]) {
-      dma(k2, a.k, k_lds[sl], k_swz, koff);
-      dma(nx, a.v, v_lds[sl ^ 1], v_swz, voff);
+    // Iteration j (stage sl = j mod 2): LDS holds K(j+1) in stage sl^1 and V(j) in stage sl;
+    // registers hold the scores of tile j. It loads K(j+2) into stage sl of K and V(j+1) into
+    // stage sl^1 of V, computes the scores of tile j+1 and folds tile j in.
+    auto iteration = [&](auto stage, f32x16 (&sc)[BN / 32], f32x16 (&sn)[BN / 32]) {
+      constexpr int sl = decltype(stage)::value;
+      __bf16* k_fill = sl ? k_lds1 : k_lds0;
+      __bf16* v_fill = sl ? v_lds0 : v_lds1;
+      const __bf16* k_read = sl ? k_lds0 : k_lds1;
+      const __bf16* v_read = sl ? v_lds1 : v_lds0;
+      dma(k2, a.k, k_fill, k_swz, koff);
+      dma(nx, a.v, v_fill, v_swz, voff);
       if (wave_live) {
         const float base = prepare(cur, sc);
         if (RA_ATTN_SETPRIO) __builtin_amdgcn_s_setprio(1);
-        fold_and_score(sc, base, v_lds[sl], sn, k_lds[sl ^ 1]);
+        fold_and_score(sc, base, v_read, sn, k_read);
         if (RA_ATTN_SETPRIO) __builtin_amdgcn_s_setprio(0);
       }
       __builtin_amdgcn_s_waitcnt(0);  // this wave's copies have landed in LDS
@@ -429,9 +455,9 @@ __global__ __launch_bounds__(NT, RA_ATTN_WAVES_PER_SIMD) void attn_bf16_kernel(c
       advance(k2);
     };
     for (int j = 0; j < total; j += 2) {
-      iteration(0, s0, s1);
+      iteration(std::integral_constant<int, 0>(), s0, s1);
       if (j + 1 >= total) break;
-      iteration(1, s1, s0);
+      iteration(std::integral_constant<int, 1>(), s1, s0);
     }
   }
 
