@@ -7,8 +7,9 @@
 // matrix of §3.4 by global position.
 //
 // Mapping onto CDNA4:
-//  * A workgroup of 4 wave64s owns BM = 128 query rows of one (batch, head); wave w owns
-//    rows 32w .. 32w+31 and lane l owns query row (l mod 32) of its wave.
+//  * A workgroup of 4 wave64s owns BM query rows of one (batch, head); each wave owns QB blocks
+//    of 32 rows and lane l owns query row (l mod 32) of each block. Every K or V operand read
+//    from LDS feeds one MFMA per block.
 //  * Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16: K tile rows
 //    from LDS are the A operand, the wave's Q rows (held in VGPRs for the whole kernel) are
 //    the B operand. The 32x32 fp32 result leaves each lane with 16 keys of its own query, so
@@ -18,9 +19,10 @@
 //    transposed A operand is read with ds_read_b64_tr_b16, which hands each lane one head-dim
 //    column of a 4-key x 16-column block; two such reads give the 8 keys that match, key for
 //    key, the order in which the score accumulator feeds the B operand.
-//  * K/V tiles (64 keys) go from HBM straight into LDS with global_load_lds_dwordx4 (each
+//  * K/V tiles (64 keys) go from HBM straight into LDS with buffer_load_dwordx4 ... lds (each
 //    lane moves 16 bytes, a wave 1 KB), so staging costs no registers and no LDS-write
-//    instructions. Rows are unpadded; the 16-byte chunks of each row are XOR-permuted by a
+//    instructions; the buffer resource covers only the tile's valid rows, so the rows of a
+//    ragged last tile arrive as zeros. Rows are unpadded; the 16-byte chunks of each row are XOR-permuted by a
 //    function of the key so that the 128-bit K reads and the transposed V reads hit distinct
 //    banks. The staging is staggered so that, while tile j is in the softmax, K of tile j+1
 //    and V of tile j are resident: the next tile's QK^T MFMAs are issued in the same block as
@@ -37,6 +39,7 @@
 #include <math.h>
 
 #include <type_traits>
+#include <utility>
 
 #include "ra_internal.h"
 
@@ -51,9 +54,12 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
+constexpr int QB = RA_ATTN_QB;    // 32-row query blocks per wave
+constexpr int WR = 32 * QB;       // query rows per wave
 constexpr int BM = kBf16BlockM;   // query rows per workgroup
 constexpr int BN = kBf16BlockN;   // keys per tile
 constexpr int NT = 64 * RA_ATTN_WAVES;  // threads per workgroup
+static_assert(BM == WR * RA_ATTN_WAVES, "block shape");
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -72,6 +78,10 @@ constexpr float kLn2 = 0.6931471805599453f;
 #ifndef RA_ATTN_WAVES_PER_SIMD
 #define RA_ATTN_WAVES_PER_SIMD 2      // occupancy target: 256 VGPRs per wave at 2, 512 at 1
 #endif
+
+// Word 3 of a raw buffer resource (untyped 32-bit data, no swizzle, no stride): reads past
+// num_records return zeros.
+constexpr int kBufferWord3 = 0x00020000;
 
 template <int D>
 struct Cfg {
@@ -121,13 +131,30 @@ __device__ inline s16x4 read_tr(const __bf16* p) {
 }
 
 // Position of the (step, tile) sequence a workgroup walks: step s of the ring, tile t of
-// that step's share, nt tiles visible in the step, the first nf of them fully visible.
+// that step's share, nt tiles visible in the step, the first nf of them fully visible. The
+// step's K/V rank and share pointers (at this workgroup's batch and head) are resolved when the
+// cursor enters the step, so the per-tile work reads no kernel arguments by index.
 struct Cursor {
-  int s, t, nt, nf;
+  int s, t, nt, nf, rank;
+  const char* kb;
+  const char* vb;
 };
 
+// Scheduling groups of one chunk of the main block: NM MFMAs, each followed by an even share
+// of the chunk's NV VALU ops and ND LDS reads.
+template <int Mask, int N>
+__device__ __forceinline__ void sched_group() {
+  if constexpr (N > 0) __builtin_amdgcn_sched_group_barrier(Mask, N, 0);
+}
+template <int NM, int NV, int ND, int... I>
+__device__ __forceinline__ void sched_chunk(std::integer_sequence<int, I...>) {
+  ((sched_group<0x008, 1>(), sched_group<0x002, (I + 1) * NV / NM - I * NV / NM>(),
+    sched_group<0x100, (I + 1) * ND / NM - I * ND / NM>()),
+   ...);
+}
+
 template <int D, class Out>
-__global__ __launch_bounds__(NT, RA_ATTN_WAVES_PER_SIMD) void attn_bf16_kernel(const AttnArgs a) {
+__global__ __launch_bounds__(NT, QB == 1 ? RA_ATTN_WAVES_PER_SIMD : 1) void attn_bf16_kernel(const AttnArgs a) {
   using C = Cfg<D>;
   // The two stages of K and V are four distinct LDS objects: the copies into one stage and the
   // reads of the other can then be told apart, so no wait for in-flight copies is inserted
@@ -150,53 +177,65 @@ __global__ __launch_bounds__(NT, RA_ATTN_WAVES_PER_SIMD) void attn_bf16_kernel(c
   const int b = bh / a.H;
   const int h = bh % a.H;
   const int q0 = qt * BM;
-  const int w0 = q0 + wave * 32;
-  const int qrow = w0 + l32;
-  const bool qvalid = qrow < a.Sq;
+  const int w0 = q0 + wave * WR;  // first row of this wave; block qb owns rows w0+32qb ..
   const bool wave_live = w0 < a.Sq;
   const int64_t rs = (int64_t)a.H * D;  // elements between consecutive sequence rows
   const float sl2 = a.scale * kLog2e;
+  auto row_of = [&](int qb) { return w0 + 32 * qb + l32; };
 
   // ---- Q rows of this wave as B operands (k = head dim), resident for the whole kernel.
-  bf16x8 qreg[D / 16];
-  {
-    const int qr = qvalid ? qrow : a.Sq - 1;
+  bf16x8 qreg[QB][D / 16];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int qr = min(row_of(qb), a.Sq - 1);
     const __bf16* qp = (const __bf16*)a.q + ((int64_t)b * a.Sq + qr) * rs + (int64_t)h * D + hh * 8;
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) qreg[ks] = *(const bf16x8*)(qp + ks * 16);
+    for (int ks = 0; ks < D / 16; ++ks) qreg[qb][ks] = *(const bf16x8*)(qp + ks * 16);
   }
 
   // ---- positions of the workgroup's, the wave's and this lane's query rows.
-  int32_t wg_qmin = 0, wg_qmax = 0, w_qmin = 0, my_qpos = -1;
+  int32_t wg_qmin = 0, wg_qmax = 0, w_qmin = 0, my_qpos[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) my_qpos[qb] = -1;
   if (a.causal) {
     wg_qmin = pos_of(a.qpos, q0);
     wg_qmax = pos_of(a.qpos, min(q0 + BM, a.Sq) - 1);
     if (wave_live) w_qmin = pos_of(a.qpos, w0);
-    if (qvalid) my_qpos = pos_of(a.qpos, qrow);
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+      if (row_of(qb) < a.Sq) my_qpos[qb] = pos_of(a.qpos, row_of(qb));
   }
 
-  // ---- running state: m (log2 domain), l (this lane half's keys), O^T accumulators.
-  float m_run = -INFINITY;
-  float l_run = 0.f;
-  f32x16 oacc[D / 32];
+  // ---- running state per row block: m (log2 domain), l (this lane half's keys), O^T.
+  float m_run[QB], l_run[QB];
+  f32x16 oacc[QB][D / 32];
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
-
-  auto state_row = [&]() { return ((int64_t)b * a.H + h) * a.Sq + qrow; };    // [B, H, S]
-  auto out_row = [&]() { return (((int64_t)b * a.Sq + qrow) * a.H + h) * D; };  // [B, S, H, D]
-  if (a.load_state && qvalid) {
-    m_run = (float)a.ws_m[state_row()];  // stored from this kernel's own fp32 values: exact
-    l_run = hh == 0 ? (float)a.ws_l[state_row()] : 0.f;
+  for (int qb = 0; qb < QB; ++qb) {
+    m_run[qb] = -INFINITY;
+    l_run[qb] = 0.f;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        f32x4 x = *(const f32x4*)(a.ws_o + out_row() + db * 32 + g * 8 + hh * 4);
+      for (int r = 0; r < 16; ++r) oacc[qb][db][r] = 0.f;
+  }
+
+  auto state_row = [&](int qb) { return ((int64_t)b * a.H + h) * a.Sq + row_of(qb); };    // [B, H, S]
+  auto out_row = [&](int qb) { return (((int64_t)b * a.Sq + row_of(qb)) * a.H + h) * D; };  // [B, S, H, D]
+  if (a.load_state) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) oacc[db][g * 4 + e] = x[e];
-      }
+    for (int qb = 0; qb < QB; ++qb) {
+      if (row_of(qb) >= a.Sq) continue;
+      m_run[qb] = (float)a.ws_m[state_row(qb)];  // stored from this kernel's own fp32 values: exact
+      l_run[qb] = hh == 0 ? (float)a.ws_l[state_row(qb)] : 0.f;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          f32x4 x = *(const f32x4*)(a.ws_o + out_row(qb) + db * 32 + g * 8 + hh * 4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) oacc[qb][db][g * 4 + e] = x[e];
+        }
+    }
   }
 
   // ---- the (step, tile) sequence this workgroup visits.
@@ -214,6 +253,16 @@ __global__ __launch_bounds__(NT, RA_ATTN_WAVES_PER_SIMD) void attn_bf16_kernel(c
     nt = (cmax + BN - 1) / BN;
     nf = cmin / BN;
   };
+  const int64_t bh_off = ((int64_t)b * a.Sk * rs + (int64_t)h * D) * 2;  // bytes to row 0 of (b, h)
+  auto enter = [&](Cursor& c, int s, int nt, int nf) {
+    c.s = s;
+    c.t = 0;
+    c.nt = nt;
+    c.nf = nf;
+    c.rank = a.kv_rank[s];
+    c.kb = (const char*)a.k[s] + bh_off;
+    c.vb = (const char*)a.v[s] + bh_off;
+  };
   // Move to the next tile; at the end the cursor stays on the last tile (a harmless dummy).
   auto advance = [&](Cursor& c) {
     if (c.t + 1 < c.nt) {
@@ -224,64 +273,55 @@ __global__ __launch_bounds__(NT, RA_ATTN_WAVES_PER_SIMD) void attn_bf16_kernel(c
       int nt, nf;
       step_tiles(s, nt, nf);
       if (nt > 0) {
-        c.s = s;
-        c.t = 0;
-        c.nt = nt;
-        c.nf = nf;
+        enter(c, s, nt, nf);
         return;
       }
     }
   };
 
   int total = 0;
-  Cursor cur = {0, 0, 0, 0};
+  Cursor cur = {0, 0, 0, 0, 0, nullptr, nullptr};
   bool found = false;
   for (int s = 0; s < a.nsteps; ++s) {
     int nt, nf;
     step_tiles(s, nt, nf);
     if (nt > 0 && !found) {
-      cur = {s, 0, nt, nf};
+      enter(cur, s, nt, nf);
       found = true;
     }
     total += nt;
   }
 
   if (total > 0) {
-    // Copy one tile (K or V of cursor c) from HBM into an LDS tile. Lane `lane` of copy i of
-    // wave w fills 16-byte slot (w*DMA + i)*64 + lane of the tile, i.e. row slot/SPR and
-    // physical chunk slot%SPR, with logical chunk (slot%SPR) ^ swizzle(row). The per-lane byte
-    // offsets into the tile are fixed, so they are computed once; only a ragged last tile
-    // (rows past Sk re-read a valid row) recomputes them.
+    // Copy one tile of K or V from HBM into an LDS tile. Lane `lane` of copy i of wave w fills
+    // 16-byte slot (w*DMA + i)*64 + lane of the tile: row r = (w*DMA + i)*RPC + lane/SPR (RPC rows
+    // per copy) and physical chunk lane%SPR, which holds logical chunk (lane%SPR) ^ swizzle(r).
+    // The V swizzle depends only on lane/SPR, so one register holds the lane's part of every V
+    // offset; the K swizzle also depends on the copy, and its XOR is formed per copy. The copies
+    // go through a buffer resource that covers only the tile's valid rows: rows past Sk of a
+    // ragged last tile read as zeros.
+    constexpr int RPC = 64 / C::SPR;  // rows per copy instruction
+    static_assert((RPC / C::RPB) % 4 == 0, "the V swizzle must repeat within one copy");
     const uint32_t rowb = (uint32_t)rs * 2;
-    uint32_t koff[C::DMA], voff[C::DMA];
+    const int lrow = lane / C::SPR, lchunk = lane % C::SPR;
+    auto tile_rsrc = [&](const char* share, int t) {
+      const int rows = min(BN, a.Sk - t * BN);
+      return __builtin_amdgcn_make_buffer_rsrc((void*)(share + (int64_t)t * BN * rowb), (short)0,
+                                               (int)((uint32_t)rows * rowb), kBufferWord3);
+    };
+    auto dma = [&](__amdgpu_buffer_rsrc_t r, __bf16* tile, bool is_k) {
+      // Formed here, at each use: kept live across the loop these would cost registers.
+      int lr = lrow, lc = lchunk;
+      asm volatile("" : "+v"(lr), "+v"(lc));
 #pragma unroll
-    for (int i = 0; i < C::DMA; ++i) {
-      const int slot = (wave * C::DMA + i) * 64 + lane;
-      const int row = slot / C::SPR;
-      koff[i] = (uint32_t)row * rowb + (uint32_t)(((slot % C::SPR) ^ C::k_swz(row)) * 16);
-      voff[i] = (uint32_t)row * rowb + (uint32_t)(((slot % C::SPR) ^ C::v_swz(row)) * 16);
-    }
-    auto dma = [&](const Cursor& c, const void* const* base, __bf16* tile, auto swz, const uint32_t* off) {
-      const char* p = (const char*)base[c.s] + (((int64_t)b * a.Sk + c.t * BN) * rs + (int64_t)h * D) * 2;
-      const int lim = a.Sk - 1 - c.t * BN;
-      if (lim >= BN - 1) {
-#pragma unroll
-        for (int i = 0; i < C::DMA; ++i)
-          __builtin_amdgcn_global_load_lds(p + off[i], (__attribute__((address_space(3))) void*)(tile + (wave * C::DMA + i) * 512),
-                                           16, 0, 0);
-      } else {
-#pragma unroll
-        for (int i = 0; i < C::DMA; ++i) {
-          const int slot = (wave * C::DMA + i) * 64 + lane;
-          const int row = slot / C::SPR;
-          const uint32_t o = (uint32_t)min(row, lim) * rowb + (uint32_t)(((slot % C::SPR) ^ swz(row)) * 16);
-          __builtin_amdgcn_global_load_lds(p + o, (__attribute__((address_space(3))) void*)(tile + (wave * C::DMA + i) * 512),
-                                           16, 0, 0);
-        }
+      for (int i = 0; i < C::DMA; ++i) {
+        const int row0 = (wave * C::DMA + i) * RPC;  // wave-uniform
+        const uint32_t lane_part = is_k ? (uint32_t)lr * rowb + (uint32_t)((lc ^ C::k_swz(row0 + lr)) * 16)
+                                        : (uint32_t)lr * rowb + (uint32_t)((lc ^ C::v_swz(lr)) * 16);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(tile + (wave * C::DMA + i) * 512),
+                                                 16, (uint32_t)row0 * rowb + lane_part, 0, 0, 0);
       }
     };
-    auto k_swz = [](int key) { return C::k_swz(key); };
-    auto v_swz = [](int key) { return C::v_swz(key); };
     // Lane-constant byte offsets of the swizzled reads (the XOR depends only on the lane).
     int kofs[D / 16];
 #pragma unroll
@@ -293,84 +333,108 @@ __global__ __launch_bounds__(NT, RA_ATTN_WAVES_PER_SIMD) void attn_bf16_kernel(c
     for (int db = 0; db < D / 32; ++db)
       vofs[db] = vrow * C::ROWB + (((4 * db + 2 * (g16 & 1) + ((jj & 3) >> 1)) ^ C::v_swz(vrow)) * 16) + (jj & 1) * 8;
 
-    auto qk = [&](const __bf16* kt, f32x16 (&s)[BN / 32]) {
+    // S^T of one tile for every row block of the wave; each K operand read feeds QB MFMAs.
+    auto qk = [&](const __bf16* kt, f32x16 (&s)[QB][BN / 32]) {
       const char* kb8 = (const char*)kt;
 #pragma unroll
       for (int kb = 0; kb < BN / 32; ++kb) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+        for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) s[qb][kb][r] = 0.f;
 #pragma unroll
         for (int ks = 0; ks < D / 16; ++ks) {
           const bf16x8 ka = *(const bf16x8*)(kb8 + kofs[ks] + kb * 32 * C::ROWB);
-          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qreg[ks], s[kb], 0, 0, 0);
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb)
+            s[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qreg[qb][ks], s[qb][kb], 0, 0, 0);
         }
       }
     };
 
     // Phase A of folding tile `c` (scores in s): causal/ragged mask where the tile needs
-    // one, the tile's row max and, where it exceeds the running max, the
-    // rescale of O and l. Returns the reference value the tile's weights are taken against.
-    auto prepare = [&](const Cursor& c, f32x16 (&s)[BN / 32]) -> float {
+    // one, each row's tile max and, where it exceeds the running max, the rescale of O and l.
+    // Sets the reference values the tile's weights are taken against.
+    auto prepare = [&](const Cursor& c, f32x16 (&s)[QB][BN / 32], float (&base)[QB]) {
       const int key0 = c.t * BN;
       bool masked = key0 + BN > a.Sk;
       Pos kvp = kv_rule;
-      kvp.rank = a.kv_rank[c.s];
+      kvp.rank = c.rank;
       if (a.causal) masked = masked || (c.t >= c.nf && w_qmin < pos_of(kvp, min(key0 + BN, a.Sk) - 1));
       if (masked) {
-        // The keys this lane's query sees form a prefix of the share: mask from its length.
-        const int32_t nvis = a.causal ? clamp32(count_le(kvp, my_qpos), 0, a.Sk) : a.Sk;
-        const int lim = nvis - key0 - hh * 4;  // compared with the lane's key offsets
+        // The keys a query sees form a prefix of the share: mask from its length.
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          const int32_t nvis = a.causal ? clamp32(count_le(kvp, my_qpos[qb]), 0, a.Sk) : a.Sk;
+          const int lim = nvis - key0 - hh * 4;  // compared with the lane's key offsets
+#pragma unroll
+          for (int kb = 0; kb < BN / 32; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int off = kb * 32 + (r >> 2) * 8 + (r & 3);
+              s[qb][kb][r] = off < lim ? s[qb][kb][r] : -INFINITY;
+            }
+        }
+      }
+      float mc[QB];
+      bool any_upd = false;
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        float mt = s[qb][0][0];
 #pragma unroll
         for (int kb = 0; kb < BN / 32; ++kb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int off = kb * 32 + (r >> 2) * 8 + (r & 3);
-            s[kb][r] = off < lim ? s[kb][r] : -INFINITY;
-          }
+          for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[qb][kb][r]);
+        mc[qb] = pair_max(mt) * sl2;
+        any_upd = any_upd || (mc[qb] > m_run[qb]);
       }
-      float mt = s[0][0];
+      if (__any(any_upd)) {
 #pragma unroll
-      for (int kb = 0; kb < BN / 32; ++kb)
+        for (int qb = 0; qb < QB; ++qb) {
+          // rows that keep their reference value (possibly -inf: no visible key yet) keep O
+          const bool upd = mc[qb] > m_run[qb];
+          const float alpha = upd ? __builtin_amdgcn_exp2f(m_run[qb] - mc[qb]) : 1.f;
+          m_run[qb] = upd ? mc[qb] : m_run[qb];
+          l_run[qb] *= alpha;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[kb][r]);
-      const float mc = pair_max(mt) * sl2;
-      const bool upd = mc > m_run;
-      if (__any(upd)) {
-        // lanes that keep their reference value (possibly -inf: no visible key yet) keep O
-        const float alpha = upd ? __builtin_amdgcn_exp2f(m_run - mc) : 1.f;
-        m_run = upd ? mc : m_run;
-        l_run *= alpha;
+          for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+            for (int r = 0; r < 16; ++r) oacc[qb][db][r] *= alpha;
+        }
       }
-      return m_run == -INFINITY ? 0.f : m_run;
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) base[qb] = m_run[qb] == -INFINITY ? 0.f : m_run[qb];
     };
 
     // Phase B, one branch-free block: the weights of the current tile (exp2), O^T += V^T P^T
     // for it, and the next tile's S^T = K Q^T, in four chunks of 16 keys so that the MFMAs of
-    // both products are issued between the VALU work of the softmax.
-    auto fold_and_score = [&](f32x16 (&sc)[BN / 32], float base, const __bf16* vt, f32x16 (&sn)[BN / 32],
-                              const __bf16* kt) {
+    // both products are issued between the VALU work of the softmax. Every V and K operand
+    // read feeds one MFMA per row block.
+    auto fold_and_score = [&](f32x16 (&sc)[QB][BN / 32], const float (&base)[QB], const __bf16* vt,
+                              f32x16 (&sn)[QB][BN / 32], const __bf16* kt) {
 #pragma unroll
-      for (int kb = 0; kb < BN / 32; ++kb)
+      for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sn[kb][r] = 0.f;
+        for (int kb = 0; kb < BN / 32; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) sn[qb][kb][r] = 0.f;
       const char* vt8 = (const char*)vt;
       const char* kt8 = (const char*)kt;
 #pragma unroll
       for (int ch = 0; ch < 2 * (BN / 32); ++ch) {
         const int kb = ch >> 1, j = ch & 1;
-        bf16x8 pb;
-        float p[8];
+        bf16x8 pb[QB];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          p[e] = __builtin_amdgcn_exp2f(fmaf(sc[kb][j * 8 + e], sl2, -base));
-          pb[e] = (__bf16)p[e];
+        for (int qb = 0; qb < QB; ++qb) {
+          float p[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            p[e] = __builtin_amdgcn_exp2f(fmaf(sc[qb][kb][j * 8 + e], sl2, -base[qb]));
+            pb[qb][e] = (__bf16)p[e];
+          }
+          // the chunk's sums as short trees (no long dependency chains through the block)
+          l_run[qb] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
         }
-        // the chunk's sums as short trees (no long dependency chains through the block)
-        l_run += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
         // O^T += V^T P^T for these 16 keys (one MFMA per 32 head-dim rows), alternating with
         // the next tile's S^T chain for key block kb, head-dim steps j*D/32 .. j*D/32 + D/32-1.
 #pragma unroll
@@ -378,41 +442,38 @@ __global__ __launch_bounds__(NT, RA_ATTN_WAVES_PER_SIMD) void attn_bf16_kernel(c
           const char* vp = vt8 + vofs[db] + (kb * 32 + j * 16) * C::ROWB;
           const s16x4 lo = read_tr((const __bf16*)vp);
           const s16x4 hi = read_tr((const __bf16*)(vp + 8 * C::ROWB));
-          const s16x8 w = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w), pb, oacc[db], 0, 0, 0);
+          const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb)
+            oacc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[qb], oacc[qb][db], 0, 0, 0);
           const int ks = j * (D / 32) + db;
           const bf16x8 ka = *(const bf16x8*)(kt8 + kofs[ks] + kb * 32 * C::ROWB);
-          sn[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qreg[ks], sn[kb], 0, 0, 0);
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb)
+            sn[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qreg[qb][ks], sn[qb][kb], 0, 0, 0);
         }
       }
 #if RA_ATTN_SCHED
       // Issue order for the block above: the first chunk's weights, a few operand reads ahead,
-      // then per MFMA a short run of VALU work (next chunk's exp2) and the reads for the MFMAs
-      // two ahead, so LDS latency and the softmax hide under the matrix-core work.
-#if RA_ATTN_SCHED == 2
-      // The next tile's score MFMAs need no softmax result: open the block with them, the first
-      // chunk's weights computed in their shadow.
-      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x100, RA_ATTN_SCHED_AHEAD, 0);
-#else
+      // then after each MFMA a short run of VALU work (the next weights) and the reads for the
+      // MFMAs ahead, so LDS latency and the softmax hide under the matrix-core work.
       __builtin_amdgcn_sched_group_barrier(0x002, 28, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, RA_ATTN_SCHED_AHEAD, 0);
-#endif
-      constexpr int kPairs = (BN / 32) * (D / 32) * 2 - (RA_ATTN_SCHED == 2 ? 2 : 0);
+      if constexpr (QB == 1) {
 #pragma unroll
-      for (int i = 0; i < kPairs; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, RA_ATTN_SCHED_VALU, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, RA_ATTN_SCHED_VALU, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        for (int i = 0; i < (BN / 32) * (D / 32) * 2; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, RA_ATTN_SCHED_VALU, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, RA_ATTN_SCHED_VALU, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+      } else {
+        // per 16-key chunk: 2*QB*(D/32) MFMAs, about 28*QB VALU ops and 3*(D/32) LDS reads
+#pragma unroll
+        for (int ch = 0; ch < 2 * (BN / 32); ++ch)
+          sched_chunk<2 * QB * (D / 32), 28 * QB, 3 * (D / 32)>(std::make_integer_sequence<int, 2 * QB * (D / 32)>());
       }
 #endif
     };
@@ -422,28 +483,29 @@ __global__ __launch_bounds__(NT, RA_ATTN_WAVES_PER_SIMD) void attn_bf16_kernel(c
     advance(nx);
     Cursor k2 = nx;
     advance(k2);
-    dma(cur, a.k, k_lds0, k_swz, koff);
-    dma(cur, a.v, v_lds0, v_swz, voff);
-    dma(nx, a.k, k_lds1, k_swz, koff);
+    dma(tile_rsrc(cur.kb, cur.t), k_lds0, true);
+    dma(tile_rsrc(cur.vb, cur.t), v_lds0, false);
+    dma(tile_rsrc(nx.kb, nx.t), k_lds1, true);
     __builtin_amdgcn_s_waitcnt(0);  // this wave's copies have landed in LDS
     __syncthreads();
 
-    f32x16 s0[BN / 32], s1[BN / 32];
+    f32x16 s0[QB][BN / 32], s1[QB][BN / 32];
     if (wave_live) qk(k_lds0, s0);
     __syncthreads();  // every wave has read K(0) before iteration 0 copies K(2) over it
     // Iteration j (stage sl = j mod 2): LDS holds K(j+1) in stage sl^1 and V(j) in stage sl;
     // registers hold the scores of tile j. It loads K(j+2) into stage sl of K and V(j+1) into
     // stage sl^1 of V, computes the scores of tile j+1 and folds tile j in.
-    auto iteration = [&](auto stage, f32x16 (&sc)[BN / 32], f32x16 (&sn)[BN / 32]) {
+    auto iteration = [&](auto stage, f32x16 (&sc)[QB][BN / 32], f32x16 (&sn)[QB][BN / 32]) {
       constexpr int sl = decltype(stage)::value;
       __bf16* k_fill = sl ? k_lds1 : k_lds0;
       __bf16* v_fill = sl ? v_lds0 : v_lds1;
       const __bf16* k_read = sl ? k_lds0 : k_lds1;
       const __bf16* v_read = sl ? v_lds1 : v_lds0;
-      dma(k2, a.k, k_fill, k_swz, koff);
-      dma(nx, a.v, v_fill, v_swz, voff);
+      dma(tile_rsrc(k2.kb, k2.t), k_fill, true);
+      dma(tile_rsrc(nx.vb, nx.t), v_fill, false);
       if (wave_live) {
-        const float base = prepare(cur, sc);
+        float base[QB];
+        prepare(cur, sc, base);
         if (RA_ATTN_SETPRIO) __builtin_amdgcn_s_setprio(1);
         fold_and_score(sc, base, v_read, sn, k_read);
         if (RA_ATTN_SETPRIO) __builtin_amdgcn_s_setprio(0);
@@ -462,34 +524,37 @@ __global__ __launch_bounds__(NT, RA_ATTN_WAVES_PER_SIMD) void attn_bf16_kernel(c
   }
 
   // ---- epilogue
-  const float l_tot = pair_sum(l_run);
-  if (!qvalid) return;
-  if (a.store_final) {
-    const bool any = l_tot > 0.f;
-    const float inv = any ? 1.f / l_tot : 0.f;
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+  for (int qb = 0; qb < QB; ++qb) {
+    const float l_tot = pair_sum(l_run[qb]);
+    if (row_of(qb) >= a.Sq) continue;
+    if (a.store_final) {
+      const bool any = l_tot > 0.f;
+      const float inv = any ? 1.f / l_tot : 0.f;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        f32x4 x;
+      for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) x[e] = oacc[db][g * 4 + e] * inv;
-        Out::store4(a.o, out_row() + db * 32 + g * 8 + hh * 4, x);
+        for (int g = 0; g < 4; ++g) {
+          f32x4 x;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) x[e] = oacc[qb][db][g * 4 + e] * inv;
+          Out::store4(a.o, out_row(qb) + db * 32 + g * 8 + hh * 4, x);
+        }
+      if (hh == 0) a.lse[state_row(qb)] = any ? (m_run[qb] + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
+    } else {
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          f32x4 x;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) x[e] = oacc[qb][db][g * 4 + e];
+          *(f32x4*)(a.ws_o + out_row(qb) + db * 32 + g * 8 + hh * 4) = x;
+        }
+      if (hh == 0) {
+        a.ws_m[state_row(qb)] = m_run[qb];
+        a.ws_l[state_row(qb)] = l_tot;
       }
-    if (hh == 0) a.lse[state_row()] = any ? (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
-  } else {
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        f32x4 x;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) x[e] = oacc[db][g * 4 + e];
-        *(f32x4*)(a.ws_o + out_row() + db * 32 + g * 8 + hh * 4) = x;
-      }
-    if (hh == 0) {
-      a.ws_m[state_row()] = m_run;
-      a.ws_l[state_row()] = l_tot;
     }
   }
 }

@@ -104,12 +104,18 @@ hipError_t launch_debug_positions(Pos p, int64_t n, int64_t* out, hipStream_t st
 hipError_t launch_debug_mask(Pos q, Pos kv, int64_t Sq, int64_t Sk, uint8_t* out,
                              hipStream_t stream);
 
-// Tile shape of the bf16 MFMA kernel: 32 query rows per wave64.
+// Tile shape of the bf16 MFMA kernel: QB blocks of 32 query rows per wave64.
 #ifndef RA_ATTN_WAVES
 #define RA_ATTN_WAVES 4
 #endif
-constexpr int kBf16BlockM = 32 * RA_ATTN_WAVES;
-constexpr int kBf16BlockN = 64;
+#ifndef RA_ATTN_QB
+#define RA_ATTN_QB 1
+#endif
+constexpr int kBf16BlockM = 32 * RA_ATTN_QB * RA_ATTN_WAVES;
+#ifndef RA_ATTN_BN
+#define RA_ATTN_BN 64
+#endif
+constexpr int kBf16BlockN = RA_ATTN_BN;
 // Tile shape of the fp32 kernel.
 constexpr int kF32BlockM = 64;
 constexpr int kF32BlockN = 32;
