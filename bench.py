@@ -31,6 +31,7 @@ METRIC = "causal-adjusted attention TFLOP/s per GPU share; % of bf16 MFMA peak"
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 FLOP/clk/CU
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 HEADLINE = "zigzag_rank3"
+SETTLE_S = 0.3              # warm-up and minimum timed span of the short secondary workloads
 KERNEL_SRC = os.path.join(ROOT, "ring_sequence_parallelism_ra_amd", "csrc", "attn_bf16.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_bf16_zigzag_rank3_traffic.json")
 
@@ -79,12 +80,25 @@ def ring_pairs(w) -> int:
     return sum(ra.share_work(q_sh, ra.Shard(w.assign, n, src, L), s, s, True)[0] for src in range(n))
 
 
-def time_calls(fn, steps, warmup):
-    """(wall ms per call over ``steps`` back-to-back calls, mean event ms per call)."""
+def time_calls(fn, steps, warmup, settle_s=0.0):
+    """(wall ms per call over ``steps`` back-to-back calls, mean event ms per call, median).
+
+    With ``settle_s`` > 0 (the short secondary workloads) the warm-up goes on for at least that
+    many seconds and at least that many seconds are timed: a call of a millisecond or two right
+    after an idle spell runs before the shader clock has ramped up (measured in-kernel: 1.38 GHz
+    on a first call vs 1.70 GHz after ~50 ms of back-to-back calls)."""
     import torch
-    for _ in range(warmup):
+    t0 = time.perf_counter()
+    n_warm = 0
+    while n_warm < warmup or time.perf_counter() - t0 < settle_s:
         fn()
+        n_warm += 1
+        if settle_s > 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
+    if settle_s > 0 and n_warm:
+        per_call = (time.perf_counter() - t0) / n_warm
+        steps = max(steps, int(settle_s / max(per_call, 1e-6)) + 1)
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     t0 = time.perf_counter()
@@ -98,7 +112,7 @@ def time_calls(fn, steps, warmup):
     return wall, sum(ev) / len(ev), sorted(ev)[len(ev) // 2]
 
 
-def bench_ring(name, steps, warmup):
+def bench_ring(name, steps, warmup, settle_s=0.0):
     import torch
 
     import ring_sequence_parallelism_ra_amd as ra
@@ -109,7 +123,7 @@ def bench_ring(name, steps, warmup):
     log(f"[bench] {name}: inputs ready in {time.perf_counter() - t0:.1f}s")
     call, o, lse = ra.prepare_ring_share(inp["q"], inp["k"], inp["v"], w.rank, assign=w.assign, causal=True)
     flops = 4 * w.head_dim * w.batch * w.heads * ring_pairs(w)
-    wall, ev_mean, ev_med = time_calls(call, steps, warmup)
+    wall, ev_mean, ev_med = time_calls(call, steps, warmup, settle_s)
     res = {"tflops": flops / (wall * 1e-3) / 1e12, "kernel_ms_mean": ev_mean, "kernel_ms_median": ev_med,
            "ms_per_step": wall, "flops": flops}
     del inp, o, lse
@@ -140,7 +154,7 @@ def bench_ulysses(steps, warmup):
         idx[0] += 1
 
     nperm = max(steps, 24)
-    wall, ev_mean, _ = time_calls(perm, nperm, 3)
+    wall, ev_mean, _ = time_calls(perm, nperm, 3, SETTLE_S)
     moved = 2 * B * L * (H // P) * D * 2  # read + write bytes per call
     perm_gbs = moved / (ev_mean * 1e-3) / 1e9
     # the local step itself: permute Q, K, V for rank 0, causal attention, inverse of O
@@ -154,9 +168,9 @@ def bench_ulysses(steps, warmup):
 
     pairs = ra.share_work(full, full, L, L, True)[0]
     flops = 4 * D * B * (H // P) * pairs
-    wall_a, ev_a, _ = time_calls(attn, steps, warmup)
+    wall_a, ev_a, _ = time_calls(attn, steps, warmup, SETTLE_S)
     o_seq = torch.empty((P, B, s_loc, H, D), dtype=torch.bfloat16, device="cuda")
-    wall_i, ev_i, _ = time_calls(lambda: ra.head2seq_permute(o, w.rank, o_seq), steps, warmup)
+    wall_i, ev_i, _ = time_calls(lambda: ra.head2seq_permute(o, w.rank, o_seq), steps, warmup, SETTLE_S)
     del stacks, outs, q, k, v, o, lse, o_seq
     torch.cuda.empty_cache()
     return {"attention_tflops": flops / (ev_a * 1e-3) / 1e12, "attention_ms": ev_a,
@@ -184,7 +198,7 @@ def bench_merge(steps, warmup):
         ra.lse_merge(*a)
         idx[0] += 1
 
-    _, ev, _ = time_calls(merge, max(steps, 12), warmup)
+    _, ev, _ = time_calls(merge, max(steps, 12), warmup, SETTLE_S)
     moved = B * S * H * (3 * 4 * D + 3 * 4)
     del sets
     torch.cuda.empty_cache()
@@ -277,7 +291,7 @@ def main():
     secondary = {}
     if not args.no_secondary:
         for name in ("contig_rank7", "striped_rank0", "striped_rank0_std4"):
-            r, _, _ = bench_ring(name, args.steps, args.warmup)
+            r, _, _ = bench_ring(name, args.steps, args.warmup, SETTLE_S)
             secondary[name] = {"tflops": round(r["tflops"], 2), "pct_bf16_peak": round(100 * r["tflops"] / PEAK_BF16_TFLOPS, 2),
                                "kernel_ms": round(r["kernel_ms_mean"], 4)}
             log(f"[bench] {name}: {r['tflops']:.1f} TFLOP/s")

@@ -313,11 +313,12 @@ __global__ __launch_bounds__(NT, QB == 1 ? RA_ATTN_WAVES_PER_SIMD : 1) void attn
       // Formed here, at each use: kept live across the loop these would cost registers.
       int lr = lrow, lc = lchunk;
       asm volatile("" : "+v"(lr), "+v"(lc));
+      const uint32_t lb = (uint32_t)lr * rowb;                          // lane's row in the copy
+      const uint32_t vl = lb + (uint32_t)((lc ^ C::v_swz(lr)) * 16);    // V: same for every copy
 #pragma unroll
       for (int i = 0; i < C::DMA; ++i) {
         const int row0 = (wave * C::DMA + i) * RPC;  // wave-uniform
-        const uint32_t lane_part = is_k ? (uint32_t)lr * rowb + (uint32_t)((lc ^ C::k_swz(row0 + lr)) * 16)
-                                        : (uint32_t)lr * rowb + (uint32_t)((lc ^ C::v_swz(lr)) * 16);
+        const uint32_t lane_part = is_k ? lb + (uint32_t)((lc ^ C::k_swz(row0 + lr)) * 16) : vl;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(tile + (wave * C::DMA + i) * 512),
                                                  16, (uint32_t)row0 * rowb + lane_part, 0, 0, 0);
       }
