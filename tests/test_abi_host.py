@@ -63,6 +63,10 @@ def test_block_attn_validation():
     assert call_block(k=ctypes.c_void_p(0x10008)) == MISALIGNED
     assert call_block(B=-1) == INVALID
     assert call_block(scale=float("nan")) == INVALID
+    # 32-bit limits: byte offsets inside a 64-row K/V tile, and the launch grid
+    assert call_block(H=1 << 18) == UNSUP                 # 2^18 heads x 128 x 2 B x 64 rows = 2^32
+    assert call_block(B=1 << 14, H=1 << 10, Sq=1 << 13, Sk=64) == UNSUP   # 128 x 2^24 workgroups
+    assert "grid" in _lib.last_error()
     # causal needs shard descriptors matching the sizes
     assert call_block(causal=1) == INVALID
     qs = Shard("zigzag", 4, 1, 256)   # share 64
