@@ -157,6 +157,16 @@ def bench_ulysses(steps, warmup):
     wall, ev_mean, _ = time_calls(perm, nperm, 3, SETTLE_S)
     moved = 2 * B * L * (H // P) * D * 2  # read + write bytes per call
     perm_gbs = moved / (ev_mean * 1e-3) / 1e9
+    # context for the HBM roofline: a plain device copy (torch) of the same 64 MiB, same rotation
+    flat = [x.view(-1)[: B * L * (H // P) * D] for x in stacks]
+    cidx = [0]
+
+    def copy():
+        outs[cidx[0] % 4].view(-1).copy_(flat[cidx[0] % 3])
+        cidx[0] += 1
+
+    _, ev_copy, _ = time_calls(copy, nperm, 3, SETTLE_S)
+    copy_gbs = moved / (ev_copy * 1e-3) / 1e9
     # the local step itself: permute Q, K, V for rank 0, causal attention, inverse of O
     q, k, v = (ra.seq2head_permute(x, w.rank) for x in stacks)
     full = ra.Shard("contiguous", 1, 0, L)
@@ -175,6 +185,7 @@ def bench_ulysses(steps, warmup):
     torch.cuda.empty_cache()
     return {"attention_tflops": flops / (ev_a * 1e-3) / 1e12, "attention_ms": ev_a,
             "permute_gbs": perm_gbs, "permute_pct_hbm": 100 * perm_gbs / PEAK_HBM_GBS,
+            "device_copy_gbs": copy_gbs,
             "inverse_permute_gbs": moved / (ev_i * 1e-3) / 1e9,
             "step_ms": 3 * moved / (perm_gbs * 1e9) * 1e3 + ev_a + ev_i}
 
@@ -297,7 +308,8 @@ def main():
             log(f"[bench] {name}: {r['tflops']:.1f} TFLOP/s")
         u = bench_ulysses(args.steps, args.warmup)
         secondary["ulysses_local"] = {k: round(v, 3) for k, v in u.items()}
-        log(f"[bench] ulysses_local: attention {u['attention_tflops']:.1f} TFLOP/s, permute {u['permute_gbs']:.0f} GB/s")
+        log(f"[bench] ulysses_local: attention {u['attention_tflops']:.1f} TFLOP/s, permute {u['permute_gbs']:.0f} GB/s "
+            f"(plain device copy of the same bytes: {u['device_copy_gbs']:.0f} GB/s)")
         m = bench_merge(args.steps, args.warmup)
         secondary["lse_merge"] = {k: (round(v, 3) if isinstance(v, float) else v) for k, v in m.items()}
         log(f"[bench] lse_merge: {m['gbs']:.0f} GB/s")

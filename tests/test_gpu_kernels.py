@@ -159,6 +159,31 @@ def test_ring_share_split_and_resume(in_dt, assign):
         check(o, lse, o_ref, lse_ref, in_dt, in_dt, what="split")
 
 
+@pytest.mark.parametrize("assign,n,l", [("contiguous", 3, 300), ("striped", 3, 300), ("zigzag", 2, 300)])
+@pytest.mark.parametrize("in_dt", ["bf16", "f32"])
+def test_ring_share_batched_ragged(assign, n, l, in_dt):
+    # B > 1, an odd head count, D = 64 and a share length that is no multiple of the tiles, run
+    # in one call and resumed over two calls through the workspace state
+    b, h, d = 2, 3, 64
+    gq, gk, gv = (gen(700 + i, (b, l, h, d), in_dt) for i in range(3))
+    qs, ks, vs = shares(gq, assign, n), shares(gk, assign, n), shares(gv, assign, n)
+    kd = [dev(x, in_dt) for x in ks]
+    vd = [dev(x, in_dt) for x in vs]
+    for r in range(n):
+        say(f"batched ragged ring {assign} N={n} L={l} rank {r} in={in_dt}")
+        qd = dev(qs[r], in_dt)
+        o1, l1 = ra.ring_share(qd, kd, vd, r, assign=assign)
+        ws = ra.ring_share_workspace(b, h, l // n, d)
+        ra.ring_share(qd, kd, vd, r, assign=assign, start_step=0, num_steps=1, ws=ws)
+        o2, l2 = ra.ring_share(qd, kd, vd, r, assign=assign, start_step=1, num_steps=n - 1, ws=ws)
+        torch.cuda.synchronize()
+        qpos = OP.positions(assign, n, r, l)
+        o_ref, lse_ref = OA.attention(values(qs[r], in_dt), values(gk, in_dt), values(gv, in_dt), qpos,
+                                      np.arange(l), True)
+        check(o1, l1, o_ref, lse_ref, in_dt, in_dt, what=f"one call rank {r}")
+        check(o2, l2, o_ref, lse_ref, in_dt, in_dt, what=f"resumed rank {r}")
+
+
 @pytest.mark.parametrize("acc_dt,blk_dt", [("f32", "f32"), ("f32", "bf16"), ("bf16", "f32"), ("bf16", "bf16")])
 @pytest.mark.parametrize("d", [128, 64, 8])
 def test_lse_merge_parity(acc_dt, blk_dt, d):
