@@ -40,7 +40,8 @@ extern "C" {
 /* Status codes. */
 #define RA_OK 0
 #define RA_ERR_INVALID_ARG (-1)  /* null pointer, rank >= N, N < 1, negative size, bad step range */
-#define RA_ERR_UNSUPPORTED (-2)  /* dtype not in {RA_F32, RA_BF16}, D not in {64, 128}, N > RA_MAX_WORLD */
+#define RA_ERR_UNSUPPORTED (-2)  /* dtype not in {RA_F32, RA_BF16}, D not in {64, 128}, N > RA_MAX_WORLD,
+                                    sizes beyond the 32-bit indexing limits (see the calls) */
 #define RA_ERR_SHAPE (-3)        /* H % P != 0, L % N != 0, L % 2N != 0 (zigzag), sizes disagree */
 #define RA_ERR_MISALIGNED (-4)   /* a device pointer is not 16-byte aligned */
 #define RA_ERR_HIP (-5)          /* a HIP launch error */
@@ -80,7 +81,9 @@ typedef struct {
  * no visible key gets O = 0 and LSE = -inf.
  * in_dtype RA_BF16 runs bf16 MFMA with fp32 accumulation; RA_F32 runs fp32 FMA.
  * D must be 64 or 128. Sq and Sk may be any non-negative size (ragged tails are masked).
- * Global lengths (q_sh->global_len, kv_sh->global_len) must be below 2^31.
+ * Global lengths (q_sh->global_len, kv_sh->global_len) must be below 2^31; B*H, Sq and Sk
+ * below 2^30; H*D*128 below 2^32 (byte offsets inside a 64-row K/V tile); ceil(Sq/64)*B*H
+ * below 2^31 (the launch grid). Beyond these limits the call returns RA_ERR_UNSUPPORTED.
  */
 int ra_block_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                       int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t D,

@@ -25,6 +25,20 @@ def _gpu():
 ASSIGNS = ["contiguous", "striped", "zigzag"]
 
 
+def test_positions_at_the_length_limit():
+    # the largest global length accepted (the last multiple of 2N = 128 below 2^31) with the
+    # largest ring: 32-bit position arithmetic must not overflow anywhere along the share
+    n = 64
+    l = ((1 << 31) - 1) // (2 * n) * (2 * n)
+    for assign in ASSIGNS:
+        for r in (0, 17, n - 1):
+            say(f"positions {assign} N={n} L={l} rank {r}")
+            got = ra.debug_positions(ra.Shard(assign, n, r, l)).cpu().numpy()
+            want = OP.positions(assign, n, r, l)
+            assert got.shape == want.shape and np.array_equal(got, want)
+            assert got.max() < l and got.min() >= 0
+
+
 @pytest.mark.parametrize("assign", ASSIGNS)
 @pytest.mark.parametrize("n,l", [(1, 64), (4, 256), (8, 8192), (8, 262144), (3, 600)])
 def test_positions_bit_exact(assign, n, l):
