@@ -159,5 +159,19 @@ def test_share_work_matches_oracle(assign, n, l, bm, bn):
             assert got == want, (r, src)
 
 
+@pytest.mark.parametrize("assign", ["contiguous", "striped", "zigzag"])
+def test_share_work_at_the_length_limit(assign):
+    # The host planner runs the kernels' own position and prefix-count functions (32-bit
+    # arithmetic): at the largest accepted global length and ring size they must still count
+    # every visible pair exactly.
+    n = 64
+    l = ((1 << 31) - 1) // (2 * n) * (2 * n)
+    s = l // n
+    r, src = 45, 12
+    got = ra.share_work(Shard(assign, n, r, l), Shard(assign, n, src, l), s, s, True, 128, 64)
+    assert got[0] == OC.visible_pairs(OP.positions(assign, n, r, l), OP.positions(assign, n, src, l))
+    assert got[1] + got[2] + got[3] == ((s + 127) // 128) * ((s + 63) // 64)
+
+
 def test_share_work_noncausal_ragged():
     assert ra.share_work(None, None, 100, 70, False, 64, 32) == (7000, 2 * 3, 0, 0)
