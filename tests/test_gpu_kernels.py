@@ -198,6 +198,30 @@ def test_ring_share_batched_ragged(assign, n, l, in_dt):
         check(o2, l2, o_ref, lse_ref, in_dt, in_dt, what=f"resumed rank {r}")
 
 
+@pytest.mark.parametrize("assign", ASSIGNS)
+def test_ring_share_zero_logits_closed_form(assign):
+    # Q = 0 makes every logit 0, so the whole ring reduces to counting and averaging: the row at
+    # global position p sees exactly the p + 1 keys at positions 0..p (the N shares cover the
+    # sequence), hence LSE = ln(p + 1) and O = mean of V over positions 0..p. This pins the causal
+    # mask, the ring order and the online update on the GPU without the oracle's attention code.
+    n, l, b, h, d = 4, 4 * 256, 1, 2, 128
+    gk, gv = (gen(800 + i, (b, l, h, d), "bf16") for i in range(2))
+    gq = np.zeros((b, l, h, d), dtype=np.uint16)
+    kd = [dev(x, "bf16") for x in shares(gk, assign, n)]
+    vd = [dev(x, "bf16") for x in shares(gv, assign, n)]
+    vcum = np.cumsum(values(gv, "bf16").astype(np.float64), axis=1)  # [b, l, h, d] prefix sums
+    for r in range(n):
+        qpos = OP.positions(assign, n, r, l)
+        qd = dev(np.ascontiguousarray(gq[:, qpos]), "bf16")
+        o, lse = ra.ring_share(qd, kd, vd, r, assign=assign, out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        cnt = (qpos + 1).astype(np.float64)
+        lse_want = np.broadcast_to(np.log(cnt)[None, None, :], (b, h, qpos.size))
+        o_want = vcum[:, qpos] / cnt[None, :, None, None]
+        assert np.abs(host(lse) - lse_want).max() < 5e-6, f"rank {r} LSE"
+        assert np.abs(host(o) - o_want).max() < 2e-5, f"rank {r} O"
+
+
 @pytest.mark.parametrize("acc_dt,blk_dt", [("f32", "f32"), ("f32", "bf16"), ("bf16", "f32"), ("bf16", "bf16")])
 @pytest.mark.parametrize("d", [128, 64, 8])
 def test_lse_merge_parity(acc_dt, blk_dt, d):
