@@ -222,6 +222,23 @@ def test_ring_share_zero_logits_closed_form(assign):
         assert np.abs(host(o) - o_want).max() < 2e-5, f"rank {r} O"
 
 
+@pytest.mark.parametrize("assign", ASSIGNS)
+def test_ring_share_single_visible_key(assign):
+    # The row at global position 0 (local row 0 of rank 0 in every assignment) sees only its own
+    # key: O = v_0 and LSE = scale * q_0 . k_0, whatever the other keys hold.
+    n, l, b, h, d = 4, 4 * 128, 1, 2, 128
+    gq, gk, gv = (gen(900 + i, (b, l, h, d), "bf16") for i in range(3))
+    qpos = OP.positions(assign, n, 0, l)
+    assert qpos[0] == 0
+    o, lse = ra.ring_share(dev(np.ascontiguousarray(gq[:, qpos]), "bf16"), [dev(x, "bf16") for x in shares(gk, assign, n)],
+                           [dev(x, "bf16") for x in shares(gv, assign, n)], 0, assign=assign, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    q0, k0, v0 = (values(x, "bf16")[:, 0].astype(np.float64) for x in (gq, gk, gv))  # [b, h, d]
+    lse_want = (q0 * k0).sum(-1) / np.sqrt(d)
+    assert np.abs(host(lse)[:, :, 0] - lse_want).max() < 1e-5
+    assert np.abs(host(o)[:, 0] - v0).max() < 1e-6
+
+
 @pytest.mark.parametrize("acc_dt,blk_dt", [("f32", "f32"), ("f32", "bf16"), ("bf16", "f32"), ("bf16", "bf16")])
 @pytest.mark.parametrize("d", [128, 64, 8])
 def test_lse_merge_parity(acc_dt, blk_dt, d):
