@@ -125,6 +125,9 @@ size_t ra_ring_share_workspace_bytes(int64_t B, int64_t H, int64_t S_loc, int64_
  *   assign, causal       token assignment of the global sequence (L = N * S_loc) and
  *                        whether the causal mask by global position applies
  *   start_step, num_steps  run steps [start_step, start_step + num_steps), in ring order
+ *                        (with bf16 inputs one call folds the KV tiles of its steps in groups
+ *                        of 32 tiles, 2048 keys, taken round-robin over the steps; the result
+ *                        is the same up to rounding, and num_steps == 1 is one ring step)
  *   ws, ws_bytes         running state (size from ra_ring_share_workspace_bytes). May be
  *                        NULL when start_step == 0 and num_steps == N (the state then stays
  *                        in registers). A call that ends before step N stores the state in

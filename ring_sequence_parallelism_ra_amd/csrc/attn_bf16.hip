@@ -1,10 +1,11 @@
 // Blockwise causal attention with the online-softmax update, bf16 MFMA on gfx950.
 //
 // What is computed ([Digest] = "从 Ring Attention 到 DeepSpeed Ulysses，再到 USP 统一框架",
-// jsqmd.com): softmax(Q K^T / sqrt(d)) V (§2) of one Q share against a sequence of KV
-// shares visited in ring order (§3.1, §3.3), each KV tile folded into the running
-// (m, l, O) of every query row by the update of §3.2. Masked pairs follow the causal
-// matrix of §3.4 by global position.
+// jsqmd.com): softmax(Q K^T / sqrt(d)) V (§2) of one Q share against the KV shares of a
+// range of ring steps (§3.1, §3.3), each KV tile folded into the running (m, l, O) of every
+// query row by the update of §3.2, whose result does not depend on the order the tiles are
+// folded in (up to rounding). Masked pairs follow the causal matrix of §3.4 by global
+// position.
 //
 // Mapping onto CDNA4:
 //  * A workgroup of 4 wave64s owns BM query rows of one (batch, head); each wave owns QB blocks
@@ -73,9 +74,14 @@ constexpr float kLn2 = 0.6931471805599453f;
 #ifndef RA_ATTN_SETPRIO
 #define RA_ATTN_SETPRIO 1             // raise wave priority while issuing the main block
 #endif
+#ifndef RA_ATTN_TILE_GROUP
+#define RA_ATTN_TILE_GROUP 32         // consecutive tiles of one step visited before the next step
+#endif
 #ifndef RA_ATTN_WAVES_PER_SIMD
 #define RA_ATTN_WAVES_PER_SIMD 2      // occupancy target: 256 VGPRs per wave at 2, 512 at 1
 #endif
+
+constexpr int TG = RA_ATTN_TILE_GROUP;
 
 // Word 3 of a raw buffer resource (untyped 32-bit data, no swizzle, no stride): reads past
 // num_records return zeros.
@@ -128,10 +134,9 @@ __device__ inline s16x4 read_tr(const __bf16* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p));
 }
 
-// Position of the (step, tile) sequence a workgroup walks: step s of the ring, tile t of
-// that step's share, nt tiles visible in the step, the first nf of them fully visible. The
-// step's K/V rank and share pointers (at this workgroup's batch and head) are resolved when the
-// cursor enters the step, so the per-tile work reads no kernel arguments by index.
+// Position in the (step, tile) sequence a workgroup walks: tile t of the share of ring step s,
+// whose first nf tiles are fully visible to the workgroup; the step's K/V rank and its share
+// pointers at the workgroup's batch and head.
 struct Cursor {
   int s, t, nt, nf, rank;
   const char* kb;
@@ -236,59 +241,74 @@ __global__ __launch_bounds__(NT, QB == 1 ? RA_ATTN_WAVES_PER_SIMD : 1) void attn
     }
   }
 
-  // ---- the (step, tile) sequence this workgroup visits.
+  // ---- the (step, tile) sequence this workgroup visits. Tiles are taken in groups of TG
+  // consecutive tiles, round-robin over the call's steps: tiles [0, TG) of every step (in step
+  // order), then tiles [TG, 2 TG) of every step that still has visible tiles, and so on. The
+  // fold is order-independent up to rounding. Taking whole shares one after another lets
+  // concurrent workgroups of a head drift onto different shares when their visible prefixes
+  // differ in length (short shares, e.g. striped ones), and their K/V tiles then miss in L2;
+  // the round-robin keeps them on the same tiles. Lane s of every wave describes step s:
+  // visible tiles, fully visible tiles, K/V rank, share pointers.
   const Pos kv_rule = make_pos(a.kv_assign, a.kv_world, 0, a.kv_len);  // rank set per step
-  auto step_tiles = [&](int s, int& nt, int& nf) {
-    if (!a.causal) {
-      nt = (a.Sk + BN - 1) / BN;
-      nf = a.Sk / BN;
-      return;
-    }
-    Pos kp = kv_rule;
-    kp.rank = a.kv_rank[s];
-    const int32_t cmax = clamp32(count_le(kp, wg_qmax), 0, a.Sk);
-    const int32_t cmin = clamp32(count_le(kp, wg_qmin), 0, a.Sk);
-    nt = (cmax + BN - 1) / BN;
-    nf = cmin / BN;
-  };
   const int64_t bh_off = ((int64_t)b * a.Sk * rs + (int64_t)h * D) * 2;  // bytes to row 0 of (b, h)
-  auto enter = [&](Cursor& c, int s, int nt, int nf) {
+  int st_nt = 0, st_nf = 0, st_rank = 0;
+  uint32_t st_k0 = 0, st_k1 = 0, st_v0 = 0, st_v1 = 0;
+  for (int s = 0; s < a.nsteps; ++s) {
+    if (lane == s) {
+      const uint64_t kp = (uint64_t)(uintptr_t)a.k[s] + (uint64_t)bh_off;
+      const uint64_t vp = (uint64_t)(uintptr_t)a.v[s] + (uint64_t)bh_off;
+      st_rank = a.kv_rank[s];
+      st_k0 = (uint32_t)kp, st_k1 = (uint32_t)(kp >> 32);
+      st_v0 = (uint32_t)vp, st_v1 = (uint32_t)(vp >> 32);
+    }
+  }
+  if (lane < a.nsteps) {
+    if (a.causal) {
+      Pos kp = kv_rule;
+      kp.rank = st_rank;
+      const int32_t cmax = clamp32(count_le(kp, wg_qmax), 0, a.Sk);
+      const int32_t cmin = clamp32(count_le(kp, wg_qmin), 0, a.Sk);
+      st_nt = (cmax + BN - 1) / BN;
+      st_nf = cmin / BN;
+    } else {
+      st_nt = (a.Sk + BN - 1) / BN;
+      st_nf = a.Sk / BN;
+    }
+  }
+  auto set_step = [&](Cursor& c, int s, int t) {
+    c.t = t;
+    if (s == c.s && c.nt > 0) return;  // same step: nothing to look up
     c.s = s;
-    c.t = 0;
-    c.nt = nt;
-    c.nf = nf;
-    c.rank = a.kv_rank[s];
-    c.kb = (const char*)a.k[s] + bh_off;
-    c.vb = (const char*)a.v[s] + bh_off;
+    c.nt = __builtin_amdgcn_readlane(st_nt, s);
+    c.nf = __builtin_amdgcn_readlane(st_nf, s);
+    c.rank = __builtin_amdgcn_readlane(st_rank, s);
+    c.kb = (const char*)(uintptr_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)st_k1, s) << 32) |
+                                    (uint32_t)__builtin_amdgcn_readlane((int)st_k0, s));
+    c.vb = (const char*)(uintptr_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)st_v1, s) << 32) |
+                                    (uint32_t)__builtin_amdgcn_readlane((int)st_v0, s));
   };
   // Move to the next tile; at the end the cursor stays on the last tile (a harmless dummy).
   auto advance = [&](Cursor& c) {
-    if (c.t + 1 < c.nt) {
+    if ((c.t + 1) % TG != 0 && c.t + 1 < c.nt) {  // inside a group of TG tiles of one step
       ++c.t;
       return;
     }
-    for (int s = c.s + 1; s < a.nsteps; ++s) {
-      int nt, nf;
-      step_tiles(s, nt, nf);
-      if (nt > 0) {
-        enter(c, s, nt, nf);
-        return;
-      }
+    const int g0 = c.t / TG * TG;
+    const uint64_t later = c.s >= 63 ? 0ull : (~0ull << (c.s + 1));
+    const uint64_t same_g = __builtin_amdgcn_ballot_w64(st_nt > g0) & later;
+    if (same_g) {
+      set_step(c, __builtin_ctzll(same_g), g0);
+      return;
     }
+    const uint64_t next_g = __builtin_amdgcn_ballot_w64(st_nt > g0 + TG);
+    if (next_g) set_step(c, __builtin_ctzll(next_g), g0 + TG);
   };
 
   int total = 0;
-  Cursor cur = {0, 0, 0, 0, 0, nullptr, nullptr};
-  bool found = false;
-  for (int s = 0; s < a.nsteps; ++s) {
-    int nt, nf;
-    step_tiles(s, nt, nf);
-    if (nt > 0 && !found) {
-      enter(cur, s, nt, nf);
-      found = true;
-    }
-    total += nt;
-  }
+  for (int s = 0; s < a.nsteps; ++s) total += __builtin_amdgcn_readlane(st_nt, s);
+  Cursor cur = {-1, 0, 0, 0, 0, nullptr, nullptr};
+  const uint64_t first = __builtin_amdgcn_ballot_w64(st_nt > 0);
+  if (first) set_step(cur, __builtin_ctzll(first), 0);
 
   if (total > 0) {
     // Copy one tile of K or V from HBM into an LDS tile. Lane `lane` of copy i of wave w fills
