@@ -198,6 +198,50 @@ def test_ring_share_batched_ragged(assign, n, l, in_dt):
         check(o2, l2, o_ref, lse_ref, in_dt, in_dt, what=f"resumed rank {r}")
 
 
+@pytest.mark.parametrize("assign,n,l,r", [("contiguous", 3, 7500, 2), ("striped", 2, 5000, 1),
+                                          ("zigzag", 2, 5000, 0)])
+def test_ring_share_tile_groups(assign, n, l, r):
+    # Shares of 2500 rows (40 tiles of 64 keys): the kernel folds 32-tile groups round-robin
+    # over the steps, so these runs cross a group boundary inside fully visible, partially
+    # visible and ragged steps; one call and a call resumed after the first step.
+    b, h, d = 1, 2, 64
+    gq, gk, gv = (gen(1100 + i, (b, l, h, d), "bf16") for i in range(3))
+    qs, ks, vs = shares(gq, assign, n), shares(gk, assign, n), shares(gv, assign, n)
+    kd = [dev(x, "bf16") for x in ks]
+    vd = [dev(x, "bf16") for x in vs]
+    say(f"tile groups {assign} N={n} L={l} rank {r}")
+    qd = dev(qs[r], "bf16")
+    o1, l1 = ra.ring_share(qd, kd, vd, r, assign=assign)
+    ws = ra.ring_share_workspace(b, h, l // n, d)
+    ra.ring_share(qd, kd, vd, r, assign=assign, start_step=0, num_steps=1, ws=ws)
+    o2, l2 = ra.ring_share(qd, kd, vd, r, assign=assign, start_step=1, num_steps=n - 1, ws=ws)
+    torch.cuda.synchronize()
+    qpos = OP.positions(assign, n, r, l)
+    o_ref, lse_ref = OA.attention(values(qs[r], "bf16"), values(gk, "bf16"), values(gv, "bf16"), qpos,
+                                  np.arange(l), True)
+    check(o1, l1, o_ref, lse_ref, "bf16", "bf16", what="one call")
+    check(o2, l2, o_ref, lse_ref, "bf16", "bf16", what="resumed")
+
+
+@pytest.mark.parametrize("assign", ASSIGNS)
+@pytest.mark.parametrize("causal", [True, False])
+def test_ring_share_64_steps(assign, causal):
+    # The largest ring: one step per lane of the kernel's step table, the last in lane 63.
+    n, l, b, h, d = 64, 64 * 64, 1, 2, 64
+    gq, gk, gv = (gen(1200 + i, (b, l, h, d), "bf16") for i in range(3))
+    qs, ks, vs = shares(gq, assign, n), shares(gk, assign, n), shares(gv, assign, n)
+    kd = [dev(x, "bf16") for x in ks]
+    vd = [dev(x, "bf16") for x in vs]
+    for r in (0, 37, 63):
+        say(f"64-step ring {assign} causal={causal} rank {r}")
+        o, lse = ra.ring_share(dev(qs[r], "bf16"), kd, vd, r, assign=assign, causal=causal)
+        torch.cuda.synchronize()
+        qpos = OP.positions(assign, n, r, l)
+        o_ref, lse_ref = OA.attention(values(qs[r], "bf16"), values(gk, "bf16"), values(gv, "bf16"), qpos,
+                                      np.arange(l), causal)
+        check(o, lse, o_ref, lse_ref, "bf16", "bf16", what=f"rank {r}")
+
+
 @pytest.mark.parametrize("assign", ASSIGNS)
 def test_ring_share_zero_logits_closed_form(assign):
     # Q = 0 makes every logit 0, so the whole ring reduces to counting and averaging: the row at
