@@ -61,6 +61,16 @@ def build(verbose: bool = False) -> str:
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stdout.decode(errors="replace"))
+    # A kernel whose host launch stub was not emitted only shows up as an undefined symbol of
+    # the library's own namespace (the loader would fail at import): refuse such a build.
+    nm = shutil.which("nm")
+    if nm:
+        out = subprocess.run([nm, "-D", "--undefined-only", tmp], stdout=subprocess.PIPE,
+                             stderr=subprocess.STDOUT).stdout.decode(errors="replace")
+        own = [ln.split()[-1] for ln in out.splitlines() if "_ZN2ra" in ln]
+        if own:
+            os.remove(tmp)
+            raise RuntimeError("link left library symbols undefined: " + ", ".join(own))
     os.replace(tmp, LIB)
     return LIB
 
