@@ -10,8 +10,9 @@ by the library's planner from the same position rule the kernel uses.
 
 Also reported in the same JSON line (``secondary``): the other bf16 workloads (contiguous
 rank 7 of L=8192, striped rank 0 of L=32768 at std 1 and 4, the Ulysses local step of
-L=65536 with its permutes), the LSE-merge bandwidth, the roofline of the attention kernel and
-the oracle timed on the host cores (``cpu_baseline``).
+L=65536 with its permutes, one device of a 128K-token USP mesh with Ulysses degree 4 and a
+zigzag ring of 2), the LSE-merge bandwidth, the roofline of the attention kernel and the
+oracle timed on the host cores (``cpu_baseline``).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-secondary] [--no-cpu-baseline]
 """
@@ -190,6 +191,53 @@ def bench_ulysses(steps, warmup):
             "step_ms": 3 * moved / (perm_gbs * 1e9) * 1e3 + ev_a + ev_i}
 
 
+def bench_usp(steps, warmup):
+    """One device of the USP mesh (Ulysses degree u inside a group, zigzag ring of r groups):
+    its step is the permute of its Ulysses group's Q, K and V for its head group, the ring over
+    the r groups' K/V of that head group (the other groups' permuted K/V are prepared untimed:
+    on a real mesh they arrive over the ring), and the inverse permute of O."""
+    import torch
+
+    import ring_sequence_parallelism_ra_amd as ra
+    import synth
+    w = synth.get("usp_u4r2")
+    gq, gk, gv = synth.global_qkv(w)
+    u, p, r, k, L, H, D, B = w.ulysses, w.ulysses_rank, w.world, w.rank, w.global_len, w.heads, w.head_dim, w.batch
+    n = u * r
+    pos = [ra.debug_positions(ra.Shard("zigzag", r, s, L)) for s in range(r)]
+
+    def stacks(g):
+        t = to_dev(g)
+        out = [torch.index_select(t, 1, ps).view(B, u, L // n, H, D).transpose(0, 1).contiguous() for ps in pos]
+        del t
+        return out
+
+    qs, ks, vs = stacks(gq), stacks(gk), stacks(gv)
+    del gq, gk, gv
+    kh = [ra.seq2head_permute(x, p) for x in ks]
+    vh = [ra.seq2head_permute(x, p) for x in vs]
+    qh = torch.empty_like(kh[0])
+    call, o, lse = ra.prepare_ring_share(qh, kh, vh, k, assign="zigzag", causal=True)
+    o_seq = torch.zeros_like(qs[k])
+
+    def step():
+        ra.seq2head_permute(qs[k], p, out=qh)
+        ra.seq2head_permute(ks[k], p, out=kh[k])
+        ra.seq2head_permute(vs[k], p, out=vh[k])
+        call()
+        ra.head2seq_permute(o, p, o_seq)
+
+    q_sh = ra.Shard("zigzag", r, k, L)
+    pairs = sum(ra.share_work(q_sh, ra.Shard("zigzag", r, s, L), L // r, L // r, True)[0] for s in range(r))
+    flops = 4 * D * B * (H // u) * pairs
+    _, ev_ring, _ = time_calls(call, steps, warmup, SETTLE_S)
+    _, ev_step, _ = time_calls(step, steps, warmup, SETTLE_S)
+    del qs, ks, vs, kh, vh, qh, o, lse, o_seq
+    torch.cuda.empty_cache()
+    return {"attention_tflops": flops / (ev_ring * 1e-3) / 1e12, "attention_ms": ev_ring,
+            "step_ms": ev_step, "step_tflops": flops / (ev_step * 1e-3) / 1e12}
+
+
 def bench_merge(steps, warmup):
     import torch
 
@@ -310,6 +358,10 @@ def main():
         secondary["ulysses_local"] = {k: round(v, 3) for k, v in u.items()}
         log(f"[bench] ulysses_local: attention {u['attention_tflops']:.1f} TFLOP/s, permute {u['permute_gbs']:.0f} GB/s "
             f"(plain device copy of the same bytes: {u['device_copy_gbs']:.0f} GB/s)")
+        us = bench_usp(args.steps, args.warmup)
+        secondary["usp_u4r2"] = {k: round(v, 3) for k, v in us.items()}
+        log(f"[bench] usp_u4r2: attention {us['attention_tflops']:.1f} TFLOP/s, device step {us['step_ms']:.3f} ms "
+            f"({us['step_tflops']:.1f} TFLOP/s incl. permutes)")
         m = bench_merge(args.steps, args.warmup)
         secondary["lse_merge"] = {k: (round(v, 3) if isinstance(v, float) else v) for k, v in m.items()}
         log(f"[bench] lse_merge: {m['gbs']:.0f} GB/s")

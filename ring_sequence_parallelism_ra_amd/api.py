@@ -116,6 +116,35 @@ def ring_share(q, k_shares, v_shares, rank, **kw):
     return o, lse
 
 
+def usp_local_step(q_stack, k_heads, v_heads, ulysses_rank, ring_rank, *, out=None, scale=0.0,
+                   out_dtype=None, stream=None):
+    """One device's USP attention ([Digest] §7.2: Ulysses all-to-all inside the Ulysses group,
+    zigzag ring attention across the ring groups, reverse all-to-all), with the collectives'
+    data already local. Three library calls, nothing computed here:
+
+      1. ra_seq2head_permute of q_stack [u, B, L/N, H, D] (the Q slices of the Ulysses group of
+         ring rank ``ring_rank``, in Ulysses-rank order) for head group ``ulysses_rank``:
+         Q [B, L/r, H/u, D], i.e. the ring share of ``ring_rank`` for heads
+         [ulysses_rank*H/u, (ulysses_rank+1)*H/u);
+      2. ra_ring_share over the r ring shares (zigzag, causal, global length L = r * L/r):
+         k_heads / v_heads are the r tensors [B, L/r, H/u, D] of the same head group, entry k
+         from ring rank k (each is that ring group's own step-1 permute; on several GPUs the
+         ring passes them along);
+      3. the inverse permute of O into ``out`` [u, B, L/N, H, D], writing only this head group.
+
+    Returns (out, O [B, L/r, H/u, D], LSE [B, H/u, L/r]).
+    """
+    _need(q_stack, "q_stack")
+    u, b, s, h, d = q_stack.shape
+    qh = seq2head_permute(q_stack, ulysses_rank, stream=stream)
+    o, lse = ring_share(qh, k_heads, v_heads, ring_rank, assign="zigzag", causal=True, scale=scale,
+                        out_dtype=out_dtype, stream=stream)
+    if out is None:
+        out = torch.zeros((u, b, s, h, d), dtype=o.dtype, device=q_stack.device)
+    head2seq_permute(o, ulysses_rank, out, stream=stream)
+    return out, o, lse
+
+
 def lse_merge(o_acc, lse_acc, o_blk, lse_blk, stream=None):
     """In-place merge of (o_blk, lse_blk) into (o_acc, lse_acc); see ra_lse_merge."""
     for t, nme in ((o_acc, "o_acc"), (lse_acc, "lse_acc"), (o_blk, "o_blk"), (lse_blk, "lse_blk")):

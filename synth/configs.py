@@ -1,11 +1,14 @@
-"""The five workloads the measurements and parity checks run on.
+"""The workloads the measurements and parity checks run on.
 
 Shapes follow the pages' workloads (long causal sequences, head dim 128, 16-32
 heads, 8-way sequence sharding); the values are synthetic (see ``synth``).
 Assignment names: ``contiguous`` (rank r holds one run of L/N tokens),
 ``striped`` (token t on rank t mod N), ``zigzag`` (2N chunks, rank r holds
 chunks r and 2N-1-r), ``ulysses`` (sequence-sharded input permuted to
-head-sharded, then one full-sequence causal attention).
+head-sharded, then one full-sequence causal attention). ``usp_u4r2`` is one device of a USP
+mesh (Ulysses degree u = 4 inside a group, zigzag ring of r = 2 groups, 128K tokens, as in the
+pages' 8-GPU u=4, r=2 run): ``world`` and ``rank`` are the ring degree and ring rank,
+``ulysses`` and ``ulysses_rank`` the Ulysses degree and the device's head group.
 """
 from __future__ import annotations
 
@@ -27,6 +30,8 @@ class Workload:
     dtype: str             # "bf16" or "f32" (input and accumulation-state precision)
     qk_std: float = 1.0
     sampled_rows: int = 0  # 0: full oracle; else 512-row sampled check
+    ulysses: int = 1       # USP: Ulysses degree u (the ring degree is `world`)
+    ulysses_rank: int = 0  # USP: the device's Ulysses rank (its head group)
 
     @property
     def share_len(self) -> int:
@@ -43,6 +48,8 @@ CONFIGS = {
                               sampled_rows=512),
     "zigzag_rank3": Workload("zigzag_rank3", 5, 1, 16, 128, 262144, 8, 3, "zigzag", True, "bf16",
                              sampled_rows=512),
+    "usp_u4r2": Workload("usp_u4r2", 6, 1, 32, 128, 131072, 2, 1, "zigzag", True, "bf16",
+                         sampled_rows=512, ulysses=4, ulysses_rank=2),
 }
 
 

@@ -1,7 +1,7 @@
-"""GPU parity on the five workloads at their full sizes, in the launch configuration the
+"""GPU parity on the workloads at their full sizes, in the launch configuration the
 benchmark times (one ra_ring_share call per rank share; the Ulysses permutes and one
-full-sequence causal ra_block_attn_fwd). The oracle checks every row of the small workloads
-and 512 seeded query rows (all heads) of the large ones."""
+full-sequence causal ra_block_attn_fwd; the USP device step). The oracle checks every row of
+the small workloads and 512 seeded query rows (all heads) of the large ones."""
 import numpy as np
 import pytest
 import torch
@@ -130,3 +130,33 @@ def test_ulysses_local():
     o_bits = o.cpu().view(torch.int16).numpy()
     back = OU.head2seq(o_bits, dst, np.zeros((P, w.batch, s_loc, H, D), dtype=np.int16))
     assert np.array_equal(o_seq.cpu().view(torch.int16).numpy(), back)
+
+
+def test_usp_u4r2_sampled():
+    # one device (Ulysses rank 2 of 4, ring rank 1 of 2) of the 128K-token USP mesh
+    w = synth.get("usp_u4r2")
+    gq, gk, gv = synth.global_qkv(w)
+    u, p, r, k, L, H = w.ulysses, w.ulysses_rank, w.world, w.rank, w.global_len, w.heads
+    n, hg = u * r, H // u
+    ring_pos = [OP.positions("zigzag", r, s, L) for s in range(r)]
+
+    def stack(g, pos):
+        share = g[:, pos]
+        return np.ascontiguousarray(share.reshape(w.batch, u, L // n, H, w.head_dim).transpose(1, 0, 2, 3, 4))
+
+    say("usp_u4r2: inputs ready")
+    k_heads = [ra.seq2head_permute(dev(stack(gk, pos), "bf16"), p) for pos in ring_pos]
+    v_heads = [ra.seq2head_permute(dev(stack(gv, pos), "bf16"), p) for pos in ring_pos]
+    out, o, lse = ra.usp_local_step(dev(stack(gq, ring_pos[k]), "bf16"), k_heads, v_heads, p, k)
+    torch.cuda.synchronize()
+    say("usp_u4r2: step done")
+    heads = slice(p * hg, (p + 1) * hg)
+    rows = synth.sample_rows(1000 * w.number, L // r, chunk_len=L // (2 * r))
+    q_share = np.ascontiguousarray(gq[:, ring_pos[k]][:, :, heads])
+    o_ref, lse_ref = oracle_rows(values(q_share, "bf16"), values(np.ascontiguousarray(gk[:, :, heads]), "bf16"),
+                                 values(np.ascontiguousarray(gv[:, :, heads]), "bf16"), ring_pos[k][rows], rows)
+    eo, el = check(host(o)[:, rows], host(lse)[:, :, rows], o_ref, lse_ref, "bf16", "bf16", "usp_u4r2")
+    say(f"  {len(rows)} rows x {hg} heads: max err O {eo:.3e} LSE {el:.3e}")
+    # the sequence slices hold O's rows for this head group: slice s, row i = ring-share row s*L/N + i
+    got = out[:, :, :, heads].transpose(0, 1).reshape(w.batch, L // r, hg, w.head_dim)
+    assert torch.equal(got.view(torch.int16), o.view(torch.int16))

@@ -242,6 +242,42 @@ def test_ring_share_64_steps(assign, causal):
         check(o, lse, o_ref, lse_ref, "bf16", "bf16", what=f"rank {r}")
 
 
+def usp_stack(g, ring_pos, u, n):
+    """The Ulysses group of one ring rank: that rank's ring share [B, L/r, H, D] (positions
+    ring_pos) cut into u consecutive slices of L/N rows, stacked [u, B, L/N, H, D]."""
+    b, _, h, d = g.shape
+    share = g[:, ring_pos]
+    return np.ascontiguousarray(share.reshape(b, u, share.shape[1] // u, h, d).transpose(1, 0, 2, 3, 4))
+
+
+@pytest.mark.parametrize("u,r,l,h,d", [(2, 2, 1024, 4, 64), (4, 2, 2048, 8, 128), (2, 4, 2048, 4, 64)])
+def test_usp_local_step(u, r, l, h, d):
+    # USP (Digest §7.2) on one GPU, every device of a u x r mesh: the device's head group of its
+    # ring share attends the whole sequence; its O goes back into the group's sequence slices,
+    # other heads untouched.
+    b, n, hg = 1, u * r, h // u
+    gq, gk, gv = (gen(1300 + i, (b, l, h, d), "bf16") for i in range(3))
+    ring_pos = [OP.positions("zigzag", r, k, l) for k in range(r)]
+    qst = [usp_stack(gq, p, u, n) for p in ring_pos]
+    kst = [usp_stack(gk, p, u, n) for p in ring_pos]
+    vst = [usp_stack(gv, p, u, n) for p in ring_pos]
+    for k in range(r):
+        for p in range(u):
+            say(f"usp u={u} r={r} L={l} ulysses rank {p} ring rank {k}")
+            k_heads = [ra.seq2head_permute(dev(x, "bf16"), p) for x in kst]
+            v_heads = [ra.seq2head_permute(dev(x, "bf16"), p) for x in vst]
+            fill = np.full((u, b, l // n, h, d), 0x40E0, dtype=np.uint16)  # 7.0
+            out, o, lse = ra.usp_local_step(dev(qst[k], "bf16"), k_heads, v_heads, p, k, out=dev(fill, "bf16"))
+            torch.cuda.synchronize()
+            heads = slice(p * hg, (p + 1) * hg)
+            o_ref, lse_ref = OA.attention(values(gq[:, ring_pos[k]][:, :, heads], "bf16"),
+                                          values(gk[:, :, heads], "bf16"), values(gv[:, :, heads], "bf16"),
+                                          ring_pos[k], np.arange(l), True)
+            check(o, lse, o_ref, lse_ref, "bf16", "bf16", what=f"p={p} k={k}")
+            want = OU.head2seq(o.cpu().view(torch.int16).numpy(), p, fill.view(np.int16).copy())
+            assert np.array_equal(out.cpu().view(torch.int16).numpy(), want)
+
+
 @pytest.mark.parametrize("assign", ASSIGNS)
 def test_ring_share_zero_logits_closed_form(assign):
     # Q = 0 makes every logit 0, so the whole ring reduces to counting and averaging: the row at
