@@ -20,7 +20,12 @@ Readings (the pages are silent or brief here):
   * LSE is the natural log of the sum of exp of the *scaled* logits over the
     visible keys (the merge formula of [Digest] §6 item 3 uses log and e);
   * a row with no visible key (possible for a single block, never for a whole
-    ring) gets O = 0 and LSE = -inf.
+    ring) gets O = 0 and LSE = -inf;
+  * grouped-query attention ([Digest] §5.3: GQA has fewer KV heads than query
+    heads; MQA has one): K and V carry H_kv heads with H_kv dividing H, and query
+    head h attends KV head h // (H / H_kv), i.e. each run of H / H_kv consecutive
+    query heads shares one KV head (the usual grouping; the pages do not spell it
+    out). H_kv = H is plain multi-head attention.
 """
 from __future__ import annotations
 
@@ -58,7 +63,8 @@ def attention_rows(q, k, v, mask, scale):
 
 def attention(q, k, v, qpos=None, kpos=None, causal: bool = False, scale=None,
               row_chunk: int = 256):
-    """fp64 attention of q [B, Sq, H, D] against k, v [B, Sk, H, D].
+    """fp64 attention of q [B, Sq, H, D] against k, v [B, Sk, H_kv, D] (H_kv divides H;
+    query head h uses KV head h // (H / H_kv)).
 
     ``qpos``/``kpos`` are the global positions of the rows (needed when
     ``causal``). Returns O [B, Sq, H, D] and LSE [B, H, Sq], both float64.
@@ -78,9 +84,13 @@ def attention(q, k, v, qpos=None, kpos=None, causal: bool = False, scale=None,
         assert qpos.shape == (sq,) and kpos.shape == (sk,)
     o = np.zeros((b_, sq, h_, d), dtype=np.float64)
     lse = np.zeros((b_, h_, sq), dtype=np.float64)
+    h_kv = k.shape[2]
+    if h_kv < 1 or h_ % h_kv or v.shape[2] != h_kv:
+        raise ValueError(f"KV heads {h_kv} must divide query heads {h_}")
+    group = h_ // h_kv
     for b in range(b_):
         for h in range(h_):
-            kk, vv = k[b, :, h, :], v[b, :, h, :]
+            kk, vv = k[b, :, h // group, :], v[b, :, h // group, :]
             for r0 in range(0, sq, row_chunk):
                 r1 = min(sq, r0 + row_chunk)
                 if causal:

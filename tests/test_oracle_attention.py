@@ -41,6 +41,34 @@ def test_matches_torch_sdpa(causal, assign):
     assert np.max(np.abs(lse - lse_ref)) < 1e-12
 
 
+@pytest.mark.parametrize("h,h_kv", [(4, 2), (6, 1), (8, 4), (3, 3)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_grouped_query_matches_torch_sdpa(h, h_kv, causal):
+    # GQA / MQA against torch's own grouped-query attention (enable_gqa), which shares each
+    # KV head among h / h_kv consecutive query heads
+    n, l, d = 4, 64, 16
+    qpos = P.positions("zigzag", n, 1, l)
+    kpos = np.arange(l)
+    q, k, v = rnd(7, 2, qpos.size, h, d), rnd(8, 2, l, h_kv, d), rnd(9, 2, l, h_kv, d)
+    o, lse = A.attention(q, k, v, qpos, kpos, causal)
+    mask = torch.from_numpy(A.visible(qpos, kpos, causal))
+    qt, kt, vt = (torch.from_numpy(x).permute(0, 2, 1, 3) for x in (q, k, v))
+    o_ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask, scale=1 / math.sqrt(d),
+                                                             enable_gqa=True).permute(0, 2, 1, 3).numpy()
+    assert o.shape == (2, qpos.size, h, d)
+    assert np.max(np.abs(o - o_ref)) < 1e-12
+    # each query head against its own KV head, one head at a time
+    for hq in range(h):
+        oh, lh = A.attention(q[:, :, hq:hq + 1], k[:, :, hq * h_kv // h:hq * h_kv // h + 1],
+                             v[:, :, hq * h_kv // h:hq * h_kv // h + 1], qpos, kpos, causal)
+        assert np.array_equal(oh[:, :, 0], o[:, :, hq]) and np.array_equal(lh[:, 0], lse[:, hq])
+
+
+def test_grouped_query_rejects_non_divisor():
+    with pytest.raises(ValueError):
+        A.attention(rnd(1, 1, 4, 6, 8), rnd(2, 1, 4, 4, 8), rnd(3, 1, 4, 4, 8))
+
+
 def test_matches_python_loops():
     qpos, kpos = np.array([3, 5, 9]), np.array([0, 4, 5, 8, 9, 12])
     q, k, v = rnd(4, 1, 3, 2, 5), rnd(5, 1, 6, 2, 5), rnd(6, 1, 6, 2, 5)
