@@ -9,7 +9,8 @@ causal-adjusted TFLOP/s: 4*D FLOPs per visible (query, key) pair per head, the p
 by the library's planner from the same position rule the kernel uses.
 
 Also reported in the same JSON line (``secondary``): the other bf16 workloads (contiguous
-rank 7 of L=8192, striped rank 0 of L=32768 at std 1 and 4, the Ulysses local step of
+rank 7 of L=8192, striped rank 0 of L=32768 at std 1 and 4, grouped-query attention with 64
+query heads on 8 KV heads on a zigzag ring of L=65536, the Ulysses local step of
 L=65536 with its permutes, one device of a 128K-token USP mesh with Ulysses degree 4 and a
 zigzag ring of 2), the LSE-merge bandwidth, the roofline of the attention kernel and the
 oracle timed on the host cores (``cpu_baseline``).
@@ -349,7 +350,7 @@ def main():
 
     secondary = {}
     if not args.no_secondary:
-        for name in ("contig_rank7", "striped_rank0", "striped_rank0_std4"):
+        for name in ("contig_rank7", "striped_rank0", "striped_rank0_std4", "gqa_zigzag_rank3"):
             r, _, _ = bench_ring(name, args.steps, args.warmup, SETTLE_S)
             secondary[name] = {"tflops": round(r["tflops"], 2), "pct_bf16_peak": round(100 * r["tflops"] / PEAK_BF16_TFLOPS, 2),
                                "kernel_ms": round(r["kernel_ms_mean"], 4)}

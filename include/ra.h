@@ -69,8 +69,12 @@ typedef struct {
  * ("flash_attn_block(Q_local, K, V) -> (out, lse)" in the ring loop of [Digest] §3.3;
  * the definition softmax(Q K^T / sqrt(d)) V is [Digest] §2).
  *
- *   q     [B, Sq, H, D]  in_dtype           k, v  [B, Sk, H, D]  in_dtype
+ *   q     [B, Sq, H, D]  in_dtype           k, v  [B, Sk, H_kv, D]  in_dtype
  *   o     [B, Sq, H, D]  o_dtype (output)   lse   [B, H, Sq]     fp32 (output)
+ *   H_kv: KV heads, 1 <= H_kv, H_kv dividing H (grouped-query attention: [Digest] §5.3 has
+ *     GQA models with fewer KV heads than query heads, MQA with one); query head h attends
+ *     KV head h / (H / H_kv). H_kv = H is plain multi-head attention. H_kv < 1 returns
+ *     RA_ERR_INVALID_ARG, a non-divisor RA_ERR_SHAPE (ignored when H == 0).
  *   causal: if non-zero, key j is visible to query i iff pos_kv(j) <= pos_q(i), the
  *     positions coming from q_sh / kv_sh (the mask is taken by global position,
  *     [Q14] engineering notes; diagonal included, [Digest] §3.4). Then Sq must equal
@@ -86,7 +90,7 @@ typedef struct {
  * below 2^31 (the launch grid). Beyond these limits the call returns RA_ERR_UNSUPPORTED.
  */
 int ra_block_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
-                      int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t D,
+                      int64_t B, int64_t H, int64_t H_kv, int64_t Sq, int64_t Sk, int64_t D,
                       int in_dtype, int o_dtype, int causal,
                       const ra_shard* q_sh, const ra_shard* kv_sh, float scale,
                       hipStream_t stream);
@@ -119,7 +123,7 @@ size_t ra_ring_share_workspace_bytes(int64_t B, int64_t H, int64_t S_loc, int64_
  * the running (m, l, O) by the online-softmax update of [Digest] §3.2.
  *   q                    [B, S_loc, H, D] in_dtype, rank's share
  *   k_shares, v_shares   HOST arrays of N device pointers; entry i is rank i's share
- *                        [B, S_loc, H, D] in_dtype
+ *                        [B, S_loc, H_kv, D] in_dtype (H_kv as in ra_block_attn_fwd)
  *   o, lse               outputs as in ra_block_attn_fwd, written when the last step
  *                        (start_step + num_steps == N) has run
  *   assign, causal       token assignment of the global sequence (L = N * S_loc) and
@@ -136,8 +140,8 @@ size_t ra_ring_share_workspace_bytes(int64_t B, int64_t H, int64_t S_loc, int64_
  * The result does not depend on how the N steps are split across calls, up to rounding.
  */
 int ra_ring_share(const void* q, const void* const* k_shares, const void* const* v_shares,
-                  void* o, float* lse, int64_t B, int64_t H, int64_t S_loc, int64_t D,
-                  int N, int rank, int assign, int causal, int in_dtype, int o_dtype,
+                  void* o, float* lse, int64_t B, int64_t H, int64_t H_kv, int64_t S_loc,
+                  int64_t D, int N, int rank, int assign, int causal, int in_dtype, int o_dtype,
                   float scale, int start_step, int num_steps, void* ws, size_t ws_bytes,
                   hipStream_t stream);
 

@@ -54,10 +54,10 @@ def _load():
     P, I64, I, F, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     SH = ctypes.POINTER(Shard)
     sig = {
-        "ra_block_attn_fwd": (I, [P, P, P, P, P, I64, I64, I64, I64, I64, I, I, I, SH, SH, F, P]),
+        "ra_block_attn_fwd": (I, [P, P, P, P, P, I64, I64, I64, I64, I64, I64, I, I, I, SH, SH, F, P]),
         "ra_lse_merge": (I, [P, P, P, P, I64, I64, I64, I64, I, I, P]),
         "ra_ring_share_workspace_bytes": (SZ, [I64, I64, I64, I64]),
-        "ra_ring_share": (I, [P, P, P, P, P, I64, I64, I64, I64, I, I, I, I, I, I, F, I, I, P, SZ, P]),
+        "ra_ring_share": (I, [P, P, P, P, P, I64, I64, I64, I64, I64, I, I, I, I, I, I, F, I, I, P, SZ, P]),
         "ra_seq2head_permute": (I, [P, P, I64, I64, I64, I64, I64, I, I, I, P]),
         "ra_last_error": (ctypes.c_char_p, []),
         "ra_share_work": (I, [SH, SH, I64, I64, I, I64, I64, ctypes.POINTER(I64)]),

@@ -48,19 +48,20 @@ def _shard(sh):
 
 def block_attn_fwd(q, k, v, *, causal=False, q_shard=None, kv_shard=None, scale=0.0, out_dtype=None,
                    o=None, lse=None, stream=None):
-    """O, LSE of q [B,Sq,H,D] against one KV block k, v [B,Sk,H,D]; see ra_block_attn_fwd."""
+    """O, LSE of q [B,Sq,H,D] against one KV block k, v [B,Sk,H_kv,D] (H_kv dividing H: grouped-
+    query attention); see ra_block_attn_fwd."""
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _need(t, n)
     b, sq, h, d = q.shape
-    sk = k.shape[1]
-    if k.shape != (b, sk, h, d) or v.shape != k.shape or k.dtype != q.dtype or v.dtype != q.dtype:
-        raise ValueError("k/v must be [B, Sk, H, D] with q's B, H, D and dtype")
+    sk, hkv = k.shape[1], k.shape[2]
+    if k.shape != (b, sk, hkv, d) or v.shape != k.shape or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("k/v must be [B, Sk, H_kv, D] with q's B, D and dtype")
     od = out_dtype or q.dtype
     if o is None:
         o = torch.empty((b, sq, h, d), dtype=od, device=q.device)
     if lse is None:
         lse = torch.empty((b, h, sq), dtype=torch.float32, device=q.device)
-    check(lib.ra_block_attn_fwd(_p(q), _p(k), _p(v), _p(o), _p(lse), b, h, sq, sk, d, _dt(q), _dt(o),
+    check(lib.ra_block_attn_fwd(_p(q), _p(k), _p(v), _p(o), _p(lse), b, h, hkv, sq, sk, d, _dt(q), _dt(o),
                                 1 if causal else 0, _shard(q_shard), _shard(kv_shard), float(scale),
                                 _stream(stream)))
     return o, lse
@@ -84,10 +85,11 @@ def prepare_ring_share(q, k_shares, v_shares, rank, *, assign="contiguous", caus
     n = len(k_shares)
     if len(v_shares) != n:
         raise ValueError("k_shares and v_shares differ in length")
+    hkv = k_shares[0].shape[2] if n else h
     for t in list(k_shares) + list(v_shares):
         _need(t, "share")
-        if t.shape != q.shape or t.dtype != q.dtype:
-            raise ValueError("every K/V share must match q's shape and dtype")
+        if t.shape != (b, s, hkv, d) or t.dtype != q.dtype:
+            raise ValueError("every K/V share must be [B, S_loc, H_kv, D] with q's B, S_loc, D and dtype")
     num = n - start_step if num_steps is None else num_steps
     od = out_dtype or q.dtype
     if o is None:
@@ -97,7 +99,7 @@ def prepare_ring_share(q, k_shares, v_shares, rank, *, assign="contiguous", caus
     kp = (ctypes.c_void_p * n)(*[t.data_ptr() for t in k_shares])
     vp = (ctypes.c_void_p * n)(*[t.data_ptr() for t in v_shares])
     ws_p, ws_n = (_p(ws), ws.numel()) if ws is not None else (None, 0)
-    args = (_p(q), kp, vp, _p(o), _p(lse), b, h, s, d, n, rank, ASSIGN.get(assign, assign),
+    args = (_p(q), kp, vp, _p(o), _p(lse), b, h, hkv, s, d, n, rank, ASSIGN.get(assign, assign),
             1 if causal else 0, _dt(q), _dt(o), float(scale), start_step, num, ws_p, ws_n,
             _stream(stream))
     keep = (k_shares, v_shares, ws)

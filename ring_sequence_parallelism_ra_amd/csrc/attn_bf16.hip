@@ -182,7 +182,9 @@ __global__ __launch_bounds__(NT, QB == 1 ? RA_ATTN_WAVES_PER_SIMD : 1) void attn
   const int q0 = qt * BM;
   const int w0 = q0 + wave * WR;  // first row of this wave; block qb owns rows w0+32qb ..
   const bool wave_live = w0 < a.Sq;
-  const int64_t rs = (int64_t)a.H * D;  // elements between consecutive sequence rows
+  const int64_t rs = (int64_t)a.H * D;       // elements between consecutive Q/O sequence rows
+  const int64_t rs_kv = (int64_t)a.Hkv * D;  // ... and K/V rows
+  const int hk = h / (a.H / a.Hkv);          // the KV head this query head reads (GQA/MQA)
   const float sl2 = a.scale * kLog2e;
   auto row_of = [&](int qb) { return w0 + 32 * qb + l32; };
 
@@ -250,7 +252,7 @@ __global__ __launch_bounds__(NT, QB == 1 ? RA_ATTN_WAVES_PER_SIMD : 1) void attn
   // the round-robin keeps them on the same tiles. Lane s of every wave describes step s:
   // visible tiles, fully visible tiles, K/V rank, share pointers.
   const Pos kv_rule = make_pos(a.kv_assign, a.kv_world, 0, a.kv_len);  // rank set per step
-  const int64_t bh_off = ((int64_t)b * a.Sk * rs + (int64_t)h * D) * 2;  // bytes to row 0 of (b, h)
+  const int64_t bh_off = ((int64_t)b * a.Sk * rs_kv + (int64_t)hk * D) * 2;  // bytes to K/V row 0 of (b, hk)
   int st_nt = 0, st_nf = 0, st_rank = 0;
   uint32_t st_k0 = 0, st_k1 = 0, st_v0 = 0, st_v1 = 0;
   for (int s = 0; s < a.nsteps; ++s) {
@@ -320,7 +322,7 @@ __global__ __launch_bounds__(NT, QB == 1 ? RA_ATTN_WAVES_PER_SIMD : 1) void attn
     // ragged last tile read as zeros.
     constexpr int RPC = 64 / C::SPR;  // rows per copy instruction
     static_assert((RPC / C::RPB) % 4 == 0, "the V swizzle must repeat within one copy");
-    const uint32_t rowb = (uint32_t)rs * 2;
+    const uint32_t rowb = (uint32_t)rs_kv * 2;
     const int lrow = lane / C::SPR, lchunk = lane % C::SPR;
     auto tile_rsrc = [&](const char* share, int t) {
       const int rows = min(BN, a.Sk - t * BN);

@@ -34,6 +34,8 @@ __global__ __launch_bounds__(BM) void attn_f32_kernel(const AttnArgs a) {
   const int qrow = q0 + lane;
   const bool qvalid = qrow < a.Sq;
   const int64_t rs = (int64_t)a.H * D;
+  const int64_t rs_kv = (int64_t)a.Hkv * D;  // K/V rows hold Hkv heads; query head h reads h / (H / Hkv)
+  const int hk = h / (a.H / a.Hkv);
 
   const float* qp = (const float*)a.q + ((int64_t)b * a.Sq + qrow) * rs + (int64_t)h * D;
   float* q = qs_ + lane * (D + 1);
@@ -63,15 +65,15 @@ __global__ __launch_bounds__(BM) void attn_f32_kernel(const AttnArgs a) {
     const Pos kvp = make_pos(a.kv_assign, a.kv_world, a.kv_rank[s], a.kv_len);
     int32_t nvis = a.Sk;
     if (a.causal) nvis = clamp32(count_le(kvp, wg_qmax), 0, a.Sk);
-    const float* kb = (const float*)a.k[s] + (int64_t)b * a.Sk * rs + (int64_t)h * D;
-    const float* vb = (const float*)a.v[s] + (int64_t)b * a.Sk * rs + (int64_t)h * D;
+    const float* kb = (const float*)a.k[s] + (int64_t)b * a.Sk * rs_kv + (int64_t)hk * D;
+    const float* vb = (const float*)a.v[s] + (int64_t)b * a.Sk * rs_kv + (int64_t)hk * D;
     for (int key0 = 0; key0 < nvis; key0 += BN) {
       __syncthreads();
       for (int u = lane; u < BN * D; u += BM) {
         const int j = u / D, d = u % D;
         const int key = key0 + j;
-        ks_[u] = key < a.Sk ? kb[key * rs + d] : 0.f;
-        vs_[u] = key < a.Sk ? vb[key * rs + d] : 0.f;
+        ks_[u] = key < a.Sk ? kb[key * rs_kv + d] : 0.f;
+        vs_[u] = key < a.Sk ? vb[key * rs_kv + d] : 0.f;
       }
       __syncthreads();
       double sc[BN];

@@ -69,6 +69,16 @@ int check_dims(int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t D) {
   return RA_OK;
 }
 
+// KV heads for grouped-query attention: 1 <= H_kv and H_kv divides H (H_kv = H: plain
+// multi-head; 1: multi-query). Ignored when H == 0.
+int check_kv_heads(int64_t H, int64_t H_kv) {
+  if (H == 0) return H_kv < 0 ? fail(RA_ERR_INVALID_ARG, "negative H_kv") : RA_OK;
+  if (H_kv < 1) return fail(RA_ERR_INVALID_ARG, "H_kv=%lld < 1", (long long)H_kv);
+  if (H % H_kv)
+    return fail(RA_ERR_SHAPE, "H_kv=%lld does not divide H=%lld", (long long)H_kv, (long long)H);
+  return RA_OK;
+}
+
 int launch_attn(const ra::AttnArgs& a, int D, int in_dtype, int o_dtype, hipStream_t stream) {
   hipError_t e = in_dtype == RA_BF16 ? ra::launch_attn_bf16(a, D, o_dtype, stream)
                                      : ra::launch_attn_f32(a, D, o_dtype, stream);
@@ -92,11 +102,12 @@ int ra_tile_shape(int in_dtype, int64_t D, int64_t* block_m, int64_t* block_n) {
 }
 
 int ra_block_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
-                      int64_t H, int64_t Sq, int64_t Sk, int64_t D, int in_dtype, int o_dtype,
-                      int causal, const ra_shard* q_sh, const ra_shard* kv_sh, float scale,
-                      hipStream_t stream) {
+                      int64_t H, int64_t H_kv, int64_t Sq, int64_t Sk, int64_t D, int in_dtype,
+                      int o_dtype, int causal, const ra_shard* q_sh, const ra_shard* kv_sh,
+                      float scale, hipStream_t stream) {
   int rc = check_dims(B, H, Sq, Sk, D);
   if (rc) return rc;
+  if ((rc = check_kv_heads(H, H_kv))) return rc;
   if (!dtype_ok(in_dtype) || !dtype_ok(o_dtype))
     return fail(RA_ERR_UNSUPPORTED, "dtype (%d, %d) not RA_F32/RA_BF16", in_dtype, o_dtype);
   if (causal) {
@@ -121,6 +132,7 @@ int ra_block_attn_fwd(const void* q, const void* k, const void* v, void* o, floa
   a.lse = lse;
   a.B = (int32_t)B;
   a.H = (int32_t)H;
+  a.Hkv = (int32_t)H_kv;
   a.Sq = (int32_t)Sq;
   a.Sk = (int32_t)Sk;
   a.nsteps = Sk > 0 ? 1 : 0;
@@ -143,11 +155,12 @@ size_t ra_ring_share_workspace_bytes(int64_t B, int64_t H, int64_t S_loc, int64_
 }
 
 int ra_ring_share(const void* q, const void* const* k_shares, const void* const* v_shares, void* o,
-                  float* lse, int64_t B, int64_t H, int64_t S_loc, int64_t D, int N, int rank,
-                  int assign, int causal, int in_dtype, int o_dtype, float scale, int start_step,
-                  int num_steps, void* ws, size_t ws_bytes, hipStream_t stream) {
+                  float* lse, int64_t B, int64_t H, int64_t H_kv, int64_t S_loc, int64_t D, int N,
+                  int rank, int assign, int causal, int in_dtype, int o_dtype, float scale,
+                  int start_step, int num_steps, void* ws, size_t ws_bytes, hipStream_t stream) {
   int rc = check_dims(B, H, S_loc, S_loc, D);
   if (rc) return rc;
+  if ((rc = check_kv_heads(H, H_kv))) return rc;
   if (!dtype_ok(in_dtype) || !dtype_ok(o_dtype))
     return fail(RA_ERR_UNSUPPORTED, "dtype (%d, %d) not RA_F32/RA_BF16", in_dtype, o_dtype);
   if (N < 1) return fail(RA_ERR_INVALID_ARG, "ring size N=%d < 1", N);
@@ -211,6 +224,7 @@ int ra_ring_share(const void* q, const void* const* k_shares, const void* const*
   }
   a.B = (int32_t)B;
   a.H = (int32_t)H;
+  a.Hkv = (int32_t)H_kv;
   a.Sq = (int32_t)S_loc;
   a.Sk = (int32_t)S_loc;
   a.nsteps = num_steps;

@@ -81,6 +81,7 @@ struct AttnArgs {
   double* ws_m;  // un-normalised O in fp32, running max and running sum in fp64 slots
   double* ws_l;
   int32_t B, H, Sq, Sk;
+  int32_t Hkv;          // KV heads (divides H): query head h reads KV head h / (H / Hkv)
   int32_t nsteps;
   int32_t causal;
   int32_t load_state;

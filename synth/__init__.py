@@ -1,7 +1,7 @@
 """Seeded synthetic inputs shared by the oracle side and the HIP side.
 
 This module holds data generation only: Gaussian draws from a named seed, the
-float32 -> bfloat16 storage conversion, the five workload descriptions and the
+float32 -> bfloat16 storage conversion, the workload descriptions and the
 choice of sampled query rows. It computes nothing of the attention method
 itself (no positions, no masks, no softmax), so both the oracle and the HIP
 path can take their inputs from here without sharing any of the method's
@@ -94,15 +94,18 @@ def gaussian_bf16_bits(seed: int, shape, std: float = 1.0) -> np.ndarray:
 def global_qkv(w: "Workload"):
     """Global Q, K, V of a workload, as stored (uint16 bf16 bits or float32).
 
-    Shapes are ``[B, L, H, D]``. Seeds are ``1000*w.number + {0, 1, 2}``.
+    Shapes are ``[B, L, H, D]`` for Q and ``[B, L, H_kv, D]`` for K and V. Seeds are
+    ``1000*w.number + {0, 1, 2}``.
     """
-    shape = (w.batch, w.global_len, w.heads, w.head_dim)
+    q_shape = (w.batch, w.global_len, w.heads, w.head_dim)
+    kv_shape = (w.batch, w.global_len, w.heads_kv, w.head_dim)
+    shapes = [q_shape, kv_shape, kv_shape]
     seeds = [1000 * w.number + i for i in range(3)]
     stds = [w.qk_std, w.qk_std, 1.0]
     if w.dtype == "bf16":
-        return tuple(gaussian_bf16_bits(s, shape, sd) for s, sd in zip(seeds, stds))
+        return tuple(gaussian_bf16_bits(s, sh, sd) for s, sh, sd in zip(seeds, shapes, stds))
     if w.dtype == "f32":
-        return tuple(gaussian_f32(s, shape, sd) for s, sd in zip(seeds, stds))
+        return tuple(gaussian_f32(s, sh, sd) for s, sh, sd in zip(seeds, shapes, stds))
     raise ValueError(w.dtype)
 
 

@@ -9,6 +9,8 @@ head-sharded, then one full-sequence causal attention). ``usp_u4r2`` is one devi
 mesh (Ulysses degree u = 4 inside a group, zigzag ring of r = 2 groups, 128K tokens, as in the
 pages' 8-GPU u=4, r=2 run): ``world`` and ``rank`` are the ring degree and ring rank,
 ``ulysses`` and ``ulysses_rank`` the Ulysses degree and the device's head group.
+``gqa_zigzag_rank3`` is grouped-query attention with the head counts of the pages' GQA example
+(64 query heads sharing 8 KV heads), on a 64K-token zigzag ring of 8.
 """
 from __future__ import annotations
 
@@ -32,6 +34,11 @@ class Workload:
     sampled_rows: int = 0  # 0: full oracle; else 512-row sampled check
     ulysses: int = 1       # USP: Ulysses degree u (the ring degree is `world`)
     ulysses_rank: int = 0  # USP: the device's Ulysses rank (its head group)
+    kv_heads: int = 0      # K/V heads for grouped-query attention (0: as many as query heads)
+
+    @property
+    def heads_kv(self) -> int:
+        return self.kv_heads or self.heads
 
     @property
     def share_len(self) -> int:
@@ -50,6 +57,8 @@ CONFIGS = {
                              sampled_rows=512),
     "usp_u4r2": Workload("usp_u4r2", 6, 1, 32, 128, 131072, 2, 1, "zigzag", True, "bf16",
                          sampled_rows=512, ulysses=4, ulysses_rank=2),
+    "gqa_zigzag_rank3": Workload("gqa_zigzag_rank3", 7, 1, 64, 128, 65536, 8, 3, "zigzag", True, "bf16",
+                                 sampled_rows=512, kv_heads=8),
 }
 
 

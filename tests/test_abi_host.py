@@ -52,7 +52,8 @@ def call_block(**over):
     a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=1, H=2, Sq=64, Sk=64, D=128, ind=1, od=1, causal=0,
              qs=None, ks=None, scale=0.0)
     a.update(over)
-    return lib.ra_block_attn_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["Sq"], a["Sk"],
+    hkv = a.get("Hkv", a["H"])
+    return lib.ra_block_attn_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], hkv, a["Sq"], a["Sk"],
                                  a["D"], a["ind"], a["od"], a["causal"], a["qs"], a["ks"], a["scale"], None)
 
 
@@ -63,6 +64,11 @@ def test_block_attn_validation():
     assert call_block(k=ctypes.c_void_p(0x10008)) == MISALIGNED
     assert call_block(B=-1) == INVALID
     assert call_block(scale=float("nan")) == INVALID
+    # grouped-query attention: KV heads must be >= 1 and divide the query heads
+    assert call_block(H=4, Hkv=0) == INVALID
+    assert call_block(H=6, Hkv=4) == SHAPE
+    assert "divide" in _lib.last_error()
+    assert call_block(H=4, Hkv=-1) == INVALID
     # 32-bit limits: byte offsets inside a 64-row K/V tile, and the launch grid
     assert call_block(H=1 << 18) == UNSUP                 # 2^18 heads x 128 x 2 B x 64 rows = 2^32
     assert call_block(B=1 << 14, H=1 << 10, Sq=1 << 13, Sk=64) == UNSUP   # 128 x 2^24 workgroups
@@ -88,7 +94,8 @@ def call_ring(**over):
     a = dict(q=FAKE, ks=arr, vs=arr, o=FAKE, lse=FAKE, B=1, H=2, S=64, D=128, N=n, rank=0, assign=0, causal=1,
              ind=1, od=1, scale=0.0, start=0, num=n, ws=None, wsb=0)
     a.update(over)
-    return lib.ra_ring_share(a["q"], a["ks"], a["vs"], a["o"], a["lse"], a["B"], a["H"], a["S"], a["D"], a["N"],
+    hkv = a.get("Hkv", a["H"])
+    return lib.ra_ring_share(a["q"], a["ks"], a["vs"], a["o"], a["lse"], a["B"], a["H"], hkv, a["S"], a["D"], a["N"],
                              a["rank"], a["assign"], a["causal"], a["ind"], a["od"], a["scale"], a["start"],
                              a["num"], a["ws"], a["wsb"], None)
 
@@ -111,6 +118,8 @@ def test_ring_share_validation():
     assert need == 4 * 64 * 2 * 128 + 16 * 2 * 64
     assert call_ring(start=1, num=3, ws=FAKE, wsb=need - 4) == INVALID
     assert call_ring(D=64, ind=5) == UNSUP
+    assert call_ring(H=4, Hkv=3) == SHAPE
+    assert call_ring(H=4, Hkv=0) == INVALID
     assert call_ring(B=0, q=None) == OK
 
 

@@ -101,6 +101,11 @@ def test_zigzag_rank3_sampled():
     _sampled_ring("zigzag_rank3")
 
 
+def test_gqa_zigzag_rank3_sampled():
+    # 64 query heads sharing 8 KV heads
+    _sampled_ring("gqa_zigzag_rank3")
+
+
 def test_ulysses_local():
     w = synth.get("ulysses_local")
     gq, gk, gv = synth.global_qkv(w)

@@ -242,6 +242,52 @@ def test_ring_share_64_steps(assign, causal):
         check(o, lse, o_ref, lse_ref, "bf16", "bf16", what=f"rank {r}")
 
 
+@pytest.mark.parametrize("h,h_kv", [(4, 2), (4, 1), (6, 3)])
+@pytest.mark.parametrize("in_dt", ["bf16", "f32"])
+@pytest.mark.parametrize("d", [128, 64])
+def test_block_attn_grouped_query(h, h_kv, in_dt, d):
+    # GQA / MQA: K and V carry h_kv heads; causal zigzag shards with a ragged-free share and a
+    # non-causal ragged block (200 queries, 136 keys)
+    b = 2
+    n, l = 4, 4 * 96
+    qs, ks = OP.positions("zigzag", n, 1, l), OP.positions("zigzag", n, 2, l)
+    for causal, sq, sk in ((True, l // n, l // n), (False, 200, 136)):
+        say(f"gqa block h={h} h_kv={h_kv} in={in_dt} d={d} causal={causal}")
+        q = gen(1400 + h, (b, sq, h, d), in_dt)
+        k = gen(1410 + h_kv, (b, sk, h_kv, d), in_dt)
+        v = gen(1420 + h_kv, (b, sk, h_kv, d), in_dt)
+        kw = dict(causal=True, q_shard=ra.Shard("zigzag", n, 1, l), kv_shard=ra.Shard("zigzag", n, 2, l)) if causal else {}
+        o, lse = ra.block_attn_fwd(dev(q, in_dt), dev(k, in_dt), dev(v, in_dt), **kw)
+        torch.cuda.synchronize()
+        o_ref, lse_ref = OA.attention(values(q, in_dt), values(k, in_dt), values(v, in_dt),
+                                      qs if causal else None, ks if causal else None, causal)
+        check(o, lse, o_ref, lse_ref, in_dt, in_dt, what=f"causal={causal}")
+
+
+@pytest.mark.parametrize("assign", ASSIGNS)
+@pytest.mark.parametrize("h,h_kv,in_dt", [(6, 2, "bf16"), (4, 1, "bf16"), (6, 2, "f32")])
+def test_ring_share_grouped_query(assign, h, h_kv, in_dt):
+    n, l, b, d = 4, 4 * 200, 1, 128
+    gq = gen(1500, (b, l, h, d), in_dt)
+    gk, gv = gen(1501, (b, l, h_kv, d), in_dt), gen(1502, (b, l, h_kv, d), in_dt)
+    qs, ks, vs = shares(gq, assign, n), shares(gk, assign, n), shares(gv, assign, n)
+    kd = [dev(x, in_dt) for x in ks]
+    vd = [dev(x, in_dt) for x in vs]
+    for r in (0, n - 1):
+        say(f"gqa ring {assign} h={h} h_kv={h_kv} in={in_dt} rank {r}")
+        qd = dev(qs[r], in_dt)
+        o1, l1 = ra.ring_share(qd, kd, vd, r, assign=assign)
+        ws = ra.ring_share_workspace(b, h, l // n, d)
+        ra.ring_share(qd, kd, vd, r, assign=assign, start_step=0, num_steps=2, ws=ws)
+        o2, l2 = ra.ring_share(qd, kd, vd, r, assign=assign, start_step=2, num_steps=n - 2, ws=ws)
+        torch.cuda.synchronize()
+        qpos = OP.positions(assign, n, r, l)
+        o_ref, lse_ref = OA.attention(values(qs[r], in_dt), values(gk, in_dt), values(gv, in_dt), qpos,
+                                      np.arange(l), True)
+        check(o1, l1, o_ref, lse_ref, in_dt, in_dt, what=f"one call rank {r}")
+        check(o2, l2, o_ref, lse_ref, in_dt, in_dt, what=f"resumed rank {r}")
+
+
 def usp_stack(g, ring_pos, u, n):
     """The Ulysses group of one ring rank: that rank's ring share [B, L/r, H, D] (positions
     ring_pos) cut into u consecutive slices of L/N rows, stacked [u, B, L/N, H, D]."""
