@@ -178,7 +178,12 @@ __global__ __launch_bounds__(NT, QB == 1 ? RA_ATTN_WAVES_PER_SIMD : 1) void attn
   const int bh = blockIdx.x % nbh;
   const int qt = n_qt - 1 - (int)(blockIdx.x / nbh);  // heaviest (latest) query tile first
   const int b = bh / a.H;
-  const int h = bh % a.H;
+  // Consecutive workgroups go to the 8 XCDs in turn, so head (bh mod H) runs on XCD
+  // (bh mod 8) when 8 divides H. With grouped KV heads the heads are renumbered so that each
+  // XCD takes a contiguous run of H/8 heads: the query heads sharing a KV head then share one
+  // XCD's L2 instead of each XCD reading every KV head.
+  const int hr = bh % a.H;
+  const int h = (a.Hkv < a.H && a.H % 8 == 0) ? (hr % 8) * (a.H / 8) + hr / 8 : hr;
   const int q0 = qt * BM;
   const int w0 = q0 + wave * WR;  // first row of this wave; block qb owns rows w0+32qb ..
   const bool wave_live = w0 < a.Sq;

@@ -242,10 +242,11 @@ def test_ring_share_64_steps(assign, causal):
         check(o, lse, o_ref, lse_ref, "bf16", "bf16", what=f"rank {r}")
 
 
-@pytest.mark.parametrize("h,h_kv", [(4, 2), (4, 1), (6, 3)])
+@pytest.mark.parametrize("h,h_kv", [(4, 2), (4, 1), (6, 3), (16, 4)])
 @pytest.mark.parametrize("in_dt", ["bf16", "f32"])
 @pytest.mark.parametrize("d", [128, 64])
 def test_block_attn_grouped_query(h, h_kv, in_dt, d):
+    # (16 query heads: the bf16 kernel renumbers heads across the XCDs when 8 divides H)
     # GQA / MQA: K and V carry h_kv heads; causal zigzag shards with a ragged-free share and a
     # non-causal ragged block (200 queries, 136 keys)
     b = 2
@@ -265,7 +266,7 @@ def test_block_attn_grouped_query(h, h_kv, in_dt, d):
 
 
 @pytest.mark.parametrize("assign", ASSIGNS)
-@pytest.mark.parametrize("h,h_kv,in_dt", [(6, 2, "bf16"), (4, 1, "bf16"), (6, 2, "f32")])
+@pytest.mark.parametrize("h,h_kv,in_dt", [(6, 2, "bf16"), (4, 1, "bf16"), (6, 2, "f32"), (8, 2, "bf16")])
 def test_ring_share_grouped_query(assign, h, h_kv, in_dt):
     n, l, b, d = 4, 4 * 200, 1, 128
     gq = gen(1500, (b, l, h, d), in_dt)
