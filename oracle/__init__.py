@@ -26,6 +26,8 @@ What each module follows:
     of [Digest] §5.1 (and [Notes] §3), by its index formula.
   * ``counts``     -- brute-force counts of visible (q, k) pairs and of tile
     classes, used for FLOP accounting and to pin the library's planner.
+  * ``backward``   -- dQ, dK, dV of the ``attention`` definition by the chain rule
+    (the pages train with ring attention but print no backward formulas).
 
 Every function is pinned by ``tests/test_oracle_*.py`` against values fixed by
 the pages or by mathematics (page examples, closed forms, a library routine on
