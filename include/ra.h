@@ -145,6 +145,37 @@ int ra_ring_share(const void* q, const void* const* k_shares, const void* const*
                   float scale, int start_step, int num_steps, void* ws, size_t ws_bytes,
                   hipStream_t stream);
 
+/* Bytes of workspace ra_ring_share_bwd needs: the row terms Delta [B, H, S] in fp32. */
+size_t ra_ring_share_bwd_workspace_bytes(int64_t B, int64_t H, int64_t S_loc);
+
+/*
+ * ra_ring_share_bwd -- gradients of ra_ring_share's output. The pages train with ring
+ * attention ([Digest] §3.1-§3.4) but print no backward formulas; this is the derivative of
+ * the forward definition ([Digest] §2 with the causal matrix of §3.4) using the forward's
+ * saved LSE: P = exp(scale q.k - LSE), Delta = rowsum(dO * O), dS = P (dO.v - Delta),
+ * dQ = scale dS K, dK = scale dS^T Q, dV = P^T dO.
+ *   q, o, dout           [B, S_loc, H, D] bf16: the rank's Q share, the forward output and
+ *                        the gradient of the loss with respect to it
+ *   lse                  [B, H, S_loc] fp32: the forward LSE (natural log)
+ *   k_shares, v_shares   HOST arrays of N device pointers, [B, S_loc, H_kv, D] bf16, as in
+ *                        ra_ring_share
+ *   dq                   [B, S_loc, H, D] fp32 output: gradient with respect to q
+ *   dk_shares, dv_shares HOST arrays of N device pointers, [B, S_loc, H_kv, D] fp32 outputs:
+ *                        entry i receives the gradient with respect to rank i's K and V
+ *                        share from this rank's queries (on a real ring these travel back to
+ *                        rank i and are summed over ranks); every entry is written
+ *   H_kv, assign, causal, scale  as in ra_ring_share (scale <= 0 selects 1/sqrt(D))
+ *   ws, ws_bytes         workspace, at least ra_ring_share_bwd_workspace_bytes(B, H, S_loc)
+ * in_dtype must be RA_BF16 (RA_F32 returns RA_ERR_UNSUPPORTED); D is 64 or 128; size limits
+ * and error codes as in ra_ring_share. Every ring step is taken in one call.
+ */
+int ra_ring_share_bwd(const void* q, const void* const* k_shares, const void* const* v_shares,
+                      const void* o, const float* lse, const void* dout, float* dq,
+                      float* const* dk_shares, float* const* dv_shares, int64_t B, int64_t H,
+                      int64_t H_kv, int64_t S_loc, int64_t D, int N, int rank, int assign,
+                      int causal, int in_dtype, float scale, void* ws, size_t ws_bytes,
+                      hipStream_t stream);
+
 /*
  * ra_seq2head_permute -- the local data movement of the Ulysses all-to-all ([Digest] §5.1,
  * [Notes] §3): sequence-sharded [bs, L/P, H, d] on each of P ranks to head-sharded

@@ -118,6 +118,39 @@ def ring_share(q, k_shares, v_shares, rank, **kw):
     return o, lse
 
 
+def ring_share_bwd(q, k_shares, v_shares, o, lse, dout, rank, *, assign="contiguous", causal=True,
+                   scale=0.0, stream=None):
+    """Gradients of ``ring_share``'s output: returns (dq [B,S,H,D], dk list, dv list), fp32, where
+    dk[i] / dv[i] [B,S,H_kv,D] are the gradients with respect to rank i's K/V share from this
+    rank's queries; see ra_ring_share_bwd."""
+    for t, nm in ((q, "q"), (o, "o"), (lse, "lse"), (dout, "dout")):
+        _need(t, nm)
+    b, s, h, d = q.shape
+    n = len(k_shares)
+    if len(v_shares) != n or n == 0:
+        raise ValueError("k_shares and v_shares must be non-empty and of equal length")
+    hkv = k_shares[0].shape[2]
+    for t in list(k_shares) + list(v_shares):
+        _need(t, "share")
+        if t.shape != (b, s, hkv, d) or t.dtype != q.dtype:
+            raise ValueError("every K/V share must be [B, S_loc, H_kv, D] with q's B, S_loc, D and dtype")
+    if o.shape != q.shape or dout.shape != q.shape or lse.shape != (b, h, s):
+        raise ValueError("o and dout must match q; lse must be [B, H, S_loc]")
+    dq = torch.empty((b, s, h, d), dtype=torch.float32, device=q.device)
+    dk = [torch.empty((b, s, hkv, d), dtype=torch.float32, device=q.device) for _ in range(n)]
+    dv = [torch.empty((b, s, hkv, d), dtype=torch.float32, device=q.device) for _ in range(n)]
+    ws_n = int(lib.ra_ring_share_bwd_workspace_bytes(b, h, s))
+    ws = torch.empty((max(ws_n, 16) + 3) // 4, dtype=torch.float32, device=q.device)
+    kp = (ctypes.c_void_p * n)(*[t.data_ptr() for t in k_shares])
+    vp = (ctypes.c_void_p * n)(*[t.data_ptr() for t in v_shares])
+    dkp = (ctypes.c_void_p * n)(*[t.data_ptr() for t in dk])
+    dvp = (ctypes.c_void_p * n)(*[t.data_ptr() for t in dv])
+    check(lib.ra_ring_share_bwd(_p(q), kp, vp, _p(o), _p(lse), _p(dout), _p(dq), dkp, dvp, b, h, hkv, s, d, n,
+                                rank, ASSIGN.get(assign, assign), 1 if causal else 0, _dt(q), float(scale),
+                                _p(ws), ws.numel() * 4, _stream(stream)))
+    return dq, dk, dv
+
+
 def usp_local_step(q_stack, k_heads, v_heads, ulysses_rank, ring_rank, *, out=None, scale=0.0,
                    out_dtype=None, stream=None):
     """One device's USP attention ([Digest] §7.2: Ulysses all-to-all inside the Ulysses group,

@@ -15,7 +15,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libra.so")
-SOURCES = ["ra_api.cpp", "attn_bf16.hip", "attn_f32.hip", "movement.hip"]
+SOURCES = ["ra_api.cpp", "attn_bf16.hip", "attn_f32.hip", "attn_bwd.hip", "movement.hip"]
 ARCH = "gfx950"
 
 

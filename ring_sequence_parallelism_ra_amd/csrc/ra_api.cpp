@@ -239,6 +239,80 @@ int ra_ring_share(const void* q, const void* const* k_shares, const void* const*
   return launch_attn(a, (int)D, in_dtype, o_dtype, stream);
 }
 
+size_t ra_ring_share_bwd_workspace_bytes(int64_t B, int64_t H, int64_t S_loc) {
+  if (B < 0 || H < 0 || S_loc < 0) return 0;
+  return (size_t)4 * (size_t)(B * H * S_loc);
+}
+
+int ra_ring_share_bwd(const void* q, const void* const* k_shares, const void* const* v_shares,
+                      const void* o, const float* lse, const void* dout, float* dq,
+                      float* const* dk_shares, float* const* dv_shares, int64_t B, int64_t H,
+                      int64_t H_kv, int64_t S_loc, int64_t D, int N, int rank, int assign, int causal,
+                      int in_dtype, float scale, void* ws, size_t ws_bytes, hipStream_t stream) {
+  int rc = check_dims(B, H, S_loc, S_loc, D);
+  if (rc) return rc;
+  if ((rc = check_kv_heads(H, H_kv))) return rc;
+  if (in_dtype != RA_BF16) return fail(RA_ERR_UNSUPPORTED, "backward runs on bf16 inputs only (in_dtype %d)", in_dtype);
+  if (N < 1) return fail(RA_ERR_INVALID_ARG, "ring size N=%d < 1", N);
+  if (N > RA_MAX_WORLD) return fail(RA_ERR_UNSUPPORTED, "ring size N=%d > %d", N, RA_MAX_WORLD);
+  if (rank < 0 || rank >= N) return fail(RA_ERR_INVALID_ARG, "rank %d not in [0, %d)", rank, N);
+  if (assign < RA_CONTIGUOUS || assign > RA_ZIGZAG) return fail(RA_ERR_INVALID_ARG, "unknown assignment %d", assign);
+  if (isnan(scale) || isinf(scale)) return fail(RA_ERR_INVALID_ARG, "scale is not finite");
+  const int64_t L = (int64_t)N * S_loc;
+  if (L >= ((int64_t)1 << 31)) return fail(RA_ERR_UNSUPPORTED, "global length N*S_loc = %lld >= 2^31", (long long)L);
+  if (causal && assign == RA_ZIGZAG && S_loc % 2)
+    return fail(RA_ERR_SHAPE, "zigzag needs L %% 2N == 0 (S_loc=%lld is odd)", (long long)S_loc);
+  const bool empty = B == 0 || H == 0 || S_loc == 0;
+  if (empty) return ok();
+  if (!q || !o || !lse || !dout || !dq || !k_shares || !v_shares || !dk_shares || !dv_shares)
+    return fail(RA_ERR_INVALID_ARG, "NULL tensor pointer or share array");
+  if (misaligned(q) || misaligned(o) || misaligned(lse) || misaligned(dout) || misaligned(dq))
+    return fail(RA_ERR_MISALIGNED, "tensor pointer not 16-byte aligned");
+  for (int i = 0; i < N; ++i) {
+    if (!k_shares[i] || !v_shares[i] || !dk_shares[i] || !dv_shares[i])
+      return fail(RA_ERR_INVALID_ARG, "share %d pointer is NULL", i);
+    if (misaligned(k_shares[i]) || misaligned(v_shares[i]) || misaligned(dk_shares[i]) || misaligned(dv_shares[i]))
+      return fail(RA_ERR_MISALIGNED, "share %d pointer not 16-byte aligned", i);
+  }
+  if (!ws) return fail(RA_ERR_INVALID_ARG, "workspace needed for the row terms");
+  if (misaligned(ws)) return fail(RA_ERR_MISALIGNED, "workspace not 16-byte aligned");
+  if (ws_bytes < ra_ring_share_bwd_workspace_bytes(B, H, S_loc))
+    return fail(RA_ERR_INVALID_ARG, "workspace %zu bytes < %zu needed", ws_bytes,
+                ra_ring_share_bwd_workspace_bytes(B, H, S_loc));
+
+  ra::BwdArgs a;
+  memset(&a, 0, sizeof a);
+  a.q = q;
+  a.o = o;
+  a.dout = dout;
+  a.lse = lse;
+  a.delta = (float*)ws;
+  a.dq = dq;
+  for (int s = 0; s < N; ++s) {
+    const int src = ((rank - s) % N + N) % N;  // ring order, as in the forward
+    a.k[s] = k_shares[src];
+    a.v[s] = v_shares[src];
+    a.dk[s] = dk_shares[src];
+    a.dv[s] = dv_shares[src];
+    a.kv_rank[s] = src;
+  }
+  a.B = (int32_t)B;
+  a.H = (int32_t)H;
+  a.Hkv = (int32_t)H_kv;
+  a.Sq = (int32_t)S_loc;
+  a.Sk = (int32_t)S_loc;
+  a.nsteps = N;
+  a.causal = causal ? 1 : 0;
+  a.scale = scale > 0.f ? scale : (float)(1.0 / sqrt((double)D));
+  a.qpos = ra::make_pos(assign, N, rank, L);
+  a.kv_assign = assign;
+  a.kv_world = N;
+  a.kv_len = L;
+  hipError_t e = ra::launch_attn_bwd(a, (int)D, stream);
+  if (e != hipSuccess) return fail(RA_ERR_HIP, "backward launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
 int ra_lse_merge(void* o_acc, float* lse_acc, const void* o_blk, const float* lse_blk, int64_t B,
                  int64_t H, int64_t S, int64_t D, int acc_dtype, int blk_dtype, hipStream_t stream) {
   if (B < 0 || H < 0 || S < 0 || D < 0) return fail(RA_ERR_INVALID_ARG, "negative size");

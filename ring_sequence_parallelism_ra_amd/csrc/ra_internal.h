@@ -92,7 +92,30 @@ struct AttnArgs {
   float scale;          // logit scale (natural units)
 };
 
+// Arguments of the backward launches (bf16 inputs, fp32 gradients; same layouts as AttnArgs).
+struct BwdArgs {
+  const void* q;
+  const void* o;
+  const void* dout;     // dO [B, Sq, H, D]
+  const float* lse;     // forward LSE [B, H, Sq] (natural log)
+  float* delta;         // workspace [B, H, Sq]: rowsum(dO * O)
+  float* dq;            // [B, Sq, H, D]
+  const void* k[kMaxSteps];
+  const void* v[kMaxSteps];
+  float* dk[kMaxSteps];  // [B, Sk, Hkv, D] per step's share
+  float* dv[kMaxSteps];
+  int32_t kv_rank[kMaxSteps];
+  int32_t B, H, Hkv, Sq, Sk;
+  int32_t nsteps;
+  int32_t causal;
+  Pos qpos;
+  int32_t kv_assign, kv_world;
+  int64_t kv_len;
+  float scale;
+};
+
 // Launchers (return hipError_t of the launch).
+hipError_t launch_attn_bwd(const BwdArgs& a, int D, hipStream_t stream);
 hipError_t launch_attn_bf16(const AttnArgs& a, int D, int o_dtype, hipStream_t stream);
 hipError_t launch_attn_f32(const AttnArgs& a, int D, int o_dtype, hipStream_t stream);
 hipError_t launch_lse_merge(void* o_acc, float* lse_acc, const void* o_blk, const float* lse_blk,

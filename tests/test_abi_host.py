@@ -123,6 +123,33 @@ def test_ring_share_validation():
     assert call_ring(B=0, q=None) == OK
 
 
+def call_bwd(**over):
+    n = over.pop("N", 4)
+    arr = (ctypes.c_void_p * max(n, 1))(*([0x10000] * max(n, 1)))
+    a = dict(q=FAKE, ks=arr, vs=arr, o=FAKE, lse=FAKE, do=FAKE, dq=FAKE, dks=arr, dvs=arr, B=1, H=2, Hkv=2, S=64,
+             D=128, N=n, rank=0, assign=0, causal=1, ind=1, scale=0.0, ws=FAKE, wsb=1 << 20)
+    a.update(over)
+    return lib.ra_ring_share_bwd(a["q"], a["ks"], a["vs"], a["o"], a["lse"], a["do"], a["dq"], a["dks"], a["dvs"],
+                                 a["B"], a["H"], a["Hkv"], a["S"], a["D"], a["N"], a["rank"], a["assign"], a["causal"],
+                                 a["ind"], a["scale"], a["ws"], a["wsb"], None)
+
+
+def test_ring_share_bwd_validation():
+    assert lib.ra_ring_share_bwd_workspace_bytes(2, 3, 100) == 4 * 2 * 3 * 100
+    assert call_bwd(ind=0) == UNSUP                       # fp32 inputs: forward only
+    assert call_bwd(D=96) == UNSUP
+    assert call_bwd(N=0) == INVALID
+    assert call_bwd(rank=4) == INVALID
+    assert call_bwd(Hkv=3, H=4) == SHAPE
+    assert call_bwd(assign=2, S=63) == SHAPE
+    assert call_bwd(ws=None) == INVALID
+    assert call_bwd(wsb=4 * 2 * 64 - 4) == INVALID
+    assert call_bwd(dq=ctypes.c_void_p(0x10004)) == MISALIGNED
+    nulls = (ctypes.c_void_p * 4)(0x10000, 0x10000, 0, 0x10000)
+    assert call_bwd(dvs=nulls) == INVALID
+    assert call_bwd(B=0, q=None, o=None) == OK            # empty: nothing launched
+
+
 def test_permute_validation():
     f = lib.ra_seq2head_permute
     assert f(FAKE, FAKE, 1, 4, 8, 6, 128, 1, 0, 0, None) == SHAPE          # 4 does not divide 6

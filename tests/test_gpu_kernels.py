@@ -6,6 +6,7 @@ import torch
 
 from gpu_helpers import TOL, check, dev, gen, half_ulp_bf16, host, say, shares, values
 from oracle import attention as OA
+from oracle import backward as OB
 from oracle import permute as OU
 from oracle import positions as OP
 from oracle import ring as OR
@@ -287,6 +288,53 @@ def test_ring_share_grouped_query(assign, h, h_kv, in_dt):
                                       np.arange(l), True)
         check(o1, l1, o_ref, lse_ref, in_dt, in_dt, what=f"one call rank {r}")
         check(o2, l2, o_ref, lse_ref, in_dt, in_dt, what=f"resumed rank {r}")
+
+
+# Backward tolerance, from the arithmetic: P and dS enter the matrix cores rounded to bf16
+# (relative 2^-9 each) and Delta = dO.O uses the bf16 forward output, so each gradient carries
+# errors of a few parts in 1e3 of its largest entries; 1e-2 of the largest entry leaves room
+# for the sums over up to a few thousand keys or queries.
+BWD_REL = 1e-2
+
+
+def check_grad(got, want, what, rel=BWD_REL):
+    """Normwise check of a gradient: max |got - want| <= rel * max |want| (see BWD_REL)."""
+    got = host(got) if isinstance(got, torch.Tensor) else got
+    assert np.all(np.isfinite(got)), f"{what}: non-finite"
+    scale = float(np.abs(want).max())
+    err = float(np.abs(got - want).max())
+    assert err <= rel * scale + 1e-6, f"{what}: error {err:.3e} > {rel} x {scale:.3e}"
+    return err / max(scale, 1e-30)
+
+
+
+
+@pytest.mark.parametrize("assign", ASSIGNS)
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("h,h_kv,d", [(2, 2, 128), (4, 2, 64), (4, 1, 128)])
+def test_ring_share_bwd_parity(assign, causal, h, h_kv, d):
+    # every rank of a 4-rank ring with 200-row shares (ragged against the 64- and 128-row tiles)
+    n, l, b = 4, 4 * 200, 1
+    gq, gdo = gen(1600, (b, l, h, d), "bf16"), gen(1603, (b, l, h, d), "bf16")
+    gk, gv = gen(1601, (b, l, h_kv, d), "bf16"), gen(1602, (b, l, h_kv, d), "bf16")
+    qs, ks, vs, dos = (shares(x, assign, n) for x in (gq, gk, gv, gdo))
+    kd = [dev(x, "bf16") for x in ks]
+    vd = [dev(x, "bf16") for x in vs]
+    for r in range(n):
+        say(f"ring bwd {assign} causal={causal} h={h} h_kv={h_kv} d={d} rank {r}")
+        qd, dod = dev(qs[r], "bf16"), dev(dos[r], "bf16")
+        o, lse = ra.ring_share(qd, kd, vd, r, assign=assign, causal=causal)
+        dq, dk, dv = ra.ring_share_bwd(qd, kd, vd, o, lse, dod, r, assign=assign, causal=causal)
+        torch.cuda.synchronize()
+        qpos = OP.positions(assign, n, r, l)
+        dq_ref, dk_ref, dv_ref = OB.attention_bwd(values(qs[r], "bf16"), values(gk, "bf16"), values(gv, "bf16"),
+                                                  values(dos[r], "bf16"), qpos, np.arange(l), causal)
+        worst = check_grad(dq, dq_ref, "dq")
+        for i in range(n):
+            p = OP.positions(assign, n, i, l)
+            worst = max(worst, check_grad(dk[i], dk_ref[:, p], f"dk share {i}"),
+                        check_grad(dv[i], dv_ref[:, p], f"dv share {i}"))
+        say(f"  largest error / largest entry: {worst:.2e}")
 
 
 def usp_stack(g, ring_pos, u, n):
