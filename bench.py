@@ -12,8 +12,8 @@ Also reported in the same JSON line (``secondary``): the other bf16 workloads (c
 rank 7 of L=8192, striped rank 0 of L=32768 at std 1 and 4, grouped-query attention with 64
 query heads on 8 KV heads on a zigzag ring of L=65536, the Ulysses local step of
 L=65536 with its permutes, one device of a 128K-token USP mesh with Ulysses degree 4 and a
-zigzag ring of 2), the LSE-merge bandwidth, the roofline of the attention kernel and the
-oracle timed on the host cores (``cpu_baseline``).
+zigzag ring of 2, the backward pass of the headline share), the LSE-merge bandwidth, the
+roofline of the attention kernel and the oracle timed on the host cores (``cpu_baseline``).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-secondary] [--no-cpu-baseline]
 """
@@ -239,6 +239,31 @@ def bench_usp(steps, warmup):
             "step_ms": ev_step, "step_tflops": flops / (ev_step * 1e-3) / 1e12}
 
 
+def bench_backward(steps, warmup):
+    """ra_ring_share_bwd on the headline share (dO drawn like the inputs). Algorithmic work:
+    5 matrix products per visible pair (S, dP, dV, dQ, dK) = 10*D FLOP; the kernels recompute S
+    and dP once more (14*D executed)."""
+    import torch
+
+    import ring_sequence_parallelism_ra_amd as ra
+    import synth
+    w = synth.get(HEADLINE)
+    inp, _ = ring_inputs(w)
+    do = to_dev(synth.gaussian_bf16_bits(1000 * w.number + 3, tuple(inp["q"].shape)))
+    o, lse = ra.ring_share(inp["q"], inp["k"], inp["v"], w.rank, assign=w.assign)
+
+    def step():
+        ra.ring_share_bwd(inp["q"], inp["k"], inp["v"], o, lse, do, w.rank, assign=w.assign)
+
+    pairs = ring_pairs(w)
+    flops = 10 * w.head_dim * w.batch * w.heads * pairs
+    _, ev, _ = time_calls(step, max(2, steps // 3), 1, 0.0)
+    del inp, do, o, lse
+    torch.cuda.empty_cache()
+    return {"tflops": flops / (ev * 1e-3) / 1e12, "ms": ev,
+            "pct_bf16_peak_executed": 100 * 1.4 * flops / (ev * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+
+
 def bench_merge(steps, warmup):
     import torch
 
@@ -363,6 +388,9 @@ def main():
         secondary["usp_u4r2"] = {k: round(v, 3) for k, v in us.items()}
         log(f"[bench] usp_u4r2: attention {us['attention_tflops']:.1f} TFLOP/s, device step {us['step_ms']:.3f} ms "
             f"({us['step_tflops']:.1f} TFLOP/s incl. permutes)")
+        bw = bench_backward(args.steps, args.warmup)
+        secondary["backward_zigzag_rank3"] = {k: round(v, 3) for k, v in bw.items()}
+        log(f"[bench] backward {HEADLINE}: {bw['tflops']:.1f} TFLOP/s (10*D FLOP per pair), {bw['ms']:.1f} ms")
         m = bench_merge(args.steps, args.warmup)
         secondary["lse_merge"] = {k: (round(v, 3) if isinstance(v, float) else v) for k, v in m.items()}
         log(f"[bench] lse_merge: {m['gbs']:.0f} GB/s")

@@ -9,6 +9,7 @@ import torch
 import synth
 from gpu_helpers import check, dev, host, say, shares, oracle_rows, values
 from oracle import attention as OA
+from oracle import backward as OB
 from oracle import permute as OU
 from oracle import positions as OP
 
@@ -165,3 +166,42 @@ def test_usp_u4r2_sampled():
     # the sequence slices hold O's rows for this head group: slice s, row i = ring-share row s*L/N + i
     got = out[:, :, :, heads].transpose(0, 1).reshape(w.batch, L // r, hg, w.head_dim)
     assert torch.equal(got.view(torch.int16), o.view(torch.int16))
+
+
+def test_zigzag_rank3_backward():
+    # The backward at the long zigzag share: dQ of 512 sampled rows against the oracle (each row
+    # needs only its own visible keys), and two identities of the softmax derivative over every
+    # key of every share: rows of P sum to 1 and rows of dS to 0, so per KV head the dK summed
+    # over all keys is 0 and the dV summed over all keys equals dO summed over all queries.
+    w = synth.get("zigzag_rank3")
+    gq, gk, gv = synth.global_qkv(w)
+    n, r, L, H, D = w.world, w.rank, w.global_len, w.heads, w.head_dim
+    pos = [OP.positions(w.assign, n, s, L) for s in range(n)]
+    q_share = np.ascontiguousarray(gq[:, pos[r]])
+    do_share = synth.gaussian_bf16_bits(1000 * w.number + 3, q_share.shape)
+    kd = [dev(np.ascontiguousarray(gk[:, p]), "bf16") for p in pos]
+    vd = [dev(np.ascontiguousarray(gv[:, p]), "bf16") for p in pos]
+    qd, dod = dev(q_share, "bf16"), dev(do_share, "bf16")
+    o, lse = ra.ring_share(qd, kd, vd, r, assign=w.assign)
+    dq, dk, dv = ra.ring_share_bwd(qd, kd, vd, o, lse, dod, r, assign=w.assign)
+    torch.cuda.synchronize()
+    say("zigzag_rank3 backward: kernels done")
+    rows = synth.sample_rows(1000 * w.number, w.share_len, chunk_len=L // (2 * n))
+    qpos = pos[r][rows]
+    kmax = int(qpos.max()) + 1
+    dq_ref, _, _ = OB.attention_bwd(values(q_share[:, rows], "bf16"), values(gk[:, :kmax], "bf16"),
+                                    values(gv[:, :kmax], "bf16"), values(do_share[:, rows], "bf16"), qpos,
+                                    np.arange(kmax), True)
+    got = host(dq)[:, rows]
+    err = np.abs(got - dq_ref).max() / np.abs(dq_ref).max()
+    say(f"  dQ on {len(rows)} rows x {H} heads: largest error / largest entry {err:.2e}")
+    assert err <= 1e-2
+    dk_sum = sum(host(x).sum(axis=1) for x in dk)          # [B, H_kv, D]
+    dk_abs = sum(np.abs(host(x)).sum(axis=1) for x in dk)
+    dv_sum = sum(host(x).sum(axis=1) for x in dv)
+    dv_abs = sum(np.abs(host(x)).sum(axis=1) for x in dv)
+    do_sum = values(do_share, "bf16").sum(axis=1)         # [B, H, D] (H_kv = H here)
+    e_k = np.abs(dk_sum).max() / dk_abs.max()
+    e_v = np.abs(dv_sum - do_sum).max() / dv_abs.max()
+    say(f"  sum over keys: |sum dK| / sum |dK| {e_k:.2e}; |sum dV - sum dO| / sum |dV| {e_v:.2e}")
+    assert e_k <= 1e-2 and e_v <= 1e-2
