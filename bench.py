@@ -15,7 +15,11 @@ L=65536 with its permutes, one device of a 128K-token USP mesh with Ulysses degr
 zigzag ring of 2, the backward pass of the headline share), the LSE-merge bandwidth, the
 roofline of the attention kernel and the oracle timed on the host cores (``cpu_baseline``).
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-secondary] [--no-cpu-baseline]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-secondary | --secondary a,b,...]
+                       [--no-cpu-baseline]
+
+``--secondary`` runs only the named secondary workloads (for short profiling runs); their
+names are the keys of ``secondary`` in the JSON line.
 """
 from __future__ import annotations
 
@@ -350,9 +354,16 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--secondary", default="", help="comma-separated subset of the secondary workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     args = ap.parse_args()
+    every = ("contig_rank7", "striped_rank0", "striped_rank0_std4", "gqa_zigzag_rank3", "ulysses_local", "usp_u4r2",
+             "backward_zigzag_rank3", "lse_merge")
+    chosen = () if args.no_secondary else (tuple(args.secondary.split(",")) if args.secondary else every)
+    unknown = [c for c in chosen if c not in every]
+    if unknown:
+        ap.error(f"unknown secondary workload(s) {unknown}; choose from {list(every)}")
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU's share only: this build runs on a single MI355X and has no "
@@ -374,26 +385,30 @@ def main():
                 "flops_per_launch": head["flops"]}
 
     secondary = {}
-    if not args.no_secondary:
-        for name in ("contig_rank7", "striped_rank0", "striped_rank0_std4", "gqa_zigzag_rank3"):
+    if chosen:
+        for name in [n for n in every[:4] if n in chosen]:
             r, _, _ = bench_ring(name, args.steps, args.warmup, SETTLE_S)
             secondary[name] = {"tflops": round(r["tflops"], 2), "pct_bf16_peak": round(100 * r["tflops"] / PEAK_BF16_TFLOPS, 2),
                                "kernel_ms": round(r["kernel_ms_mean"], 4)}
             log(f"[bench] {name}: {r['tflops']:.1f} TFLOP/s")
-        u = bench_ulysses(args.steps, args.warmup)
-        secondary["ulysses_local"] = {k: round(v, 3) for k, v in u.items()}
-        log(f"[bench] ulysses_local: attention {u['attention_tflops']:.1f} TFLOP/s, permute {u['permute_gbs']:.0f} GB/s "
-            f"(plain device copy of the same bytes: {u['device_copy_gbs']:.0f} GB/s)")
-        us = bench_usp(args.steps, args.warmup)
-        secondary["usp_u4r2"] = {k: round(v, 3) for k, v in us.items()}
-        log(f"[bench] usp_u4r2: attention {us['attention_tflops']:.1f} TFLOP/s, device step {us['step_ms']:.3f} ms "
-            f"({us['step_tflops']:.1f} TFLOP/s incl. permutes)")
-        bw = bench_backward(args.steps, args.warmup)
-        secondary["backward_zigzag_rank3"] = {k: round(v, 3) for k, v in bw.items()}
-        log(f"[bench] backward {HEADLINE}: {bw['tflops']:.1f} TFLOP/s (10*D FLOP per pair), {bw['ms']:.1f} ms")
-        m = bench_merge(args.steps, args.warmup)
-        secondary["lse_merge"] = {k: (round(v, 3) if isinstance(v, float) else v) for k, v in m.items()}
-        log(f"[bench] lse_merge: {m['gbs']:.0f} GB/s")
+        if "ulysses_local" in chosen:
+            u = bench_ulysses(args.steps, args.warmup)
+            secondary["ulysses_local"] = {k: round(v, 3) for k, v in u.items()}
+            log(f"[bench] ulysses_local: attention {u['attention_tflops']:.1f} TFLOP/s, permute {u['permute_gbs']:.0f} GB/s "
+                f"(plain device copy of the same bytes: {u['device_copy_gbs']:.0f} GB/s)")
+        if "usp_u4r2" in chosen:
+            us = bench_usp(args.steps, args.warmup)
+            secondary["usp_u4r2"] = {k: round(v, 3) for k, v in us.items()}
+            log(f"[bench] usp_u4r2: attention {us['attention_tflops']:.1f} TFLOP/s, device step {us['step_ms']:.3f} ms "
+                f"({us['step_tflops']:.1f} TFLOP/s incl. permutes)")
+        if "backward_zigzag_rank3" in chosen:
+            bw = bench_backward(args.steps, args.warmup)
+            secondary["backward_zigzag_rank3"] = {k: round(v, 3) for k, v in bw.items()}
+            log(f"[bench] backward {HEADLINE}: {bw['tflops']:.1f} TFLOP/s (10*D FLOP per pair), {bw['ms']:.1f} ms")
+        if "lse_merge" in chosen:
+            m = bench_merge(args.steps, args.warmup)
+            secondary["lse_merge"] = {k: (round(v, 3) if isinstance(v, float) else v) for k, v in m.items()}
+            log(f"[bench] lse_merge: {m['gbs']:.0f} GB/s")
 
     cpu = None
     if not args.no_cpu_baseline:
