@@ -12,7 +12,8 @@ Also reported in the same JSON line (``secondary``): the other bf16 workloads (c
 rank 7 of L=8192, striped rank 0 of L=32768 at std 1 and 4, grouped-query attention with 64
 query heads on 8 KV heads on a zigzag ring of L=65536, the Ulysses local step of
 L=65536 with its permutes, one device of a 128K-token USP mesh with Ulysses degree 4 and a
-zigzag ring of 2, the backward pass of the headline share), the LSE-merge bandwidth, the
+zigzag ring of 2, the backward pass of the headline share, the heaviest rank of each token
+assignment at the pages' Striped Attention sizes), the LSE-merge bandwidth, the
 roofline of the attention kernel and the oracle timed on the host cores (``cpu_baseline``).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-secondary | --secondary a,b,...]
@@ -268,6 +269,55 @@ def bench_backward(steps, warmup):
             "pct_bf16_peak_executed": 100 * 1.4 * flops / (ev * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
 
 
+def bench_balance(steps, warmup):
+    """The pages' Striped Attention comparison, projected from one GPU.
+
+    A ring of N devices finishes when its slowest rank does, so the time of the heaviest rank's
+    whole share (one ra_ring_share call over all N steps) bounds the ring's attention time. For
+    each token assignment (contiguous, striped, zigzag) this times the heaviest rank's share --
+    the rank with the most visible pairs by the library's planner -- at the pages' two sizes
+    (256K tokens on 8 devices, 786K on 16), B=1, H=16, D=128, causal, bf16 N(0,1) inputs drawn on
+    the device. The contiguous/striped ratio is the compute-only counterpart of the pages'
+    end-to-end 1.45x (256K, A100/TPUv4) and 1.65x (786K, 16x TPUv4); communication is not
+    modelled."""
+    import torch
+
+    import ring_sequence_parallelism_ra_amd as ra
+    H, D = 16, 128
+    out = {}
+    for L, n in ((262144, 8), (786432, 16)):
+        g = torch.Generator(device="cuda").manual_seed(L + n)
+        glob = [torch.randn((1, L, H, D), device="cuda", generator=g).to(torch.bfloat16) for _ in range(3)]
+        s_loc = L // n
+        res = {}
+        for assign in ("contiguous", "striped", "zigzag"):
+            sh = [ra.Shard(assign, n, r, L) for r in range(n)]
+            pairs = [sum(ra.share_work(sh[r], sh[src], s_loc, s_loc, True)[0] for src in range(n)) for r in range(n)]
+            rank = max(range(n), key=lambda r: pairs[r])
+            pos = [ra.debug_positions(x) for x in sh]
+            q = torch.index_select(glob[0], 1, pos[rank]).contiguous()
+            ks = [torch.index_select(glob[1], 1, p).contiguous() for p in pos]
+            vs = [torch.index_select(glob[2], 1, p).contiguous() for p in pos]
+            call, o, lse = ra.prepare_ring_share(q, ks, vs, rank, assign=assign, causal=True)
+            _, ev, _ = time_calls(call, steps, warmup)
+            flops = 4 * D * H * pairs[rank]
+            res[assign] = {"rank": rank, "ms": round(ev, 3), "tflops": round(flops / (ev * 1e-3) / 1e12, 1),
+                           "pairs_per_head": pairs[rank], "lightest_rank_pairs_per_head": min(pairs)}
+            del q, ks, vs, o, lse, call
+            torch.cuda.empty_cache()
+        c = res["contiguous"]
+        res["striped_speedup"] = round(c["ms"] / res["striped"]["ms"], 3)
+        res["zigzag_speedup"] = round(c["ms"] / res["zigzag"]["ms"], 3)
+        res["striped_pair_ratio"] = round(c["pairs_per_head"] / res["striped"]["pairs_per_head"], 3)
+        out[f"L{L}_N{n}"] = res
+        del glob
+        torch.cuda.empty_cache()
+    out["pages_context"] = ("Striped over contiguous Ring Attention, end to end: 1.45x at 256K tokens "
+                            "(A100 / TPUv4), 1.65x at 786K tokens (16x TPUv4); other hardware, with "
+                            "communication; context only")
+    return out
+
+
 def bench_merge(steps, warmup):
     import torch
 
@@ -359,7 +409,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     args = ap.parse_args()
     every = ("contig_rank7", "striped_rank0", "striped_rank0_std4", "gqa_zigzag_rank3", "ulysses_local", "usp_u4r2",
-             "backward_zigzag_rank3", "lse_merge")
+             "backward_zigzag_rank3", "lse_merge", "striped_vs_contiguous")
     chosen = () if args.no_secondary else (tuple(args.secondary.split(",")) if args.secondary else every)
     unknown = [c for c in chosen if c not in every]
     if unknown:
@@ -405,6 +455,14 @@ def main():
             bw = bench_backward(args.steps, args.warmup)
             secondary["backward_zigzag_rank3"] = {k: round(v, 3) for k, v in bw.items()}
             log(f"[bench] backward {HEADLINE}: {bw['tflops']:.1f} TFLOP/s (10*D FLOP per pair), {bw['ms']:.1f} ms")
+        if "striped_vs_contiguous" in chosen:
+            sb = bench_balance(min(args.steps, 3), 1)
+            secondary["striped_vs_contiguous"] = sb
+            for k, v in sb.items():
+                if isinstance(v, dict):
+                    log(f"[bench] striped_vs_contiguous {k}: heaviest-rank share contiguous {v['contiguous']['ms']:.1f} ms, "
+                        f"striped {v['striped']['ms']:.1f} ms, zigzag {v['zigzag']['ms']:.1f} ms -> striped "
+                        f"{v['striped_speedup']}x, zigzag {v['zigzag_speedup']}x over contiguous")
         if "lse_merge" in chosen:
             m = bench_merge(args.steps, args.warmup)
             secondary["lse_merge"] = {k: (round(v, 3) if isinstance(v, float) else v) for k, v in m.items()}
