@@ -42,6 +42,10 @@ constexpr int NT = 64 * NW;  // threads per workgroup
 constexpr int QT = 128;      // dq_kernel: query rows per workgroup (32 per wave)
 constexpr int KT = 128;      // dkdv_kernel: keys per workgroup (32 per wave)
 constexpr int BT = 64;       // rows of a streamed tile (keys in dq_kernel, queries in dkdv_kernel)
+static_assert(KT % BT == 0, "the dK/dV kernel stages its V rows as whole tiles");
+#ifndef RA_DKDV_WG_PER_CU
+#define RA_DKDV_WG_PER_CU 2  // dK/dV workgroups resident per CU (registers per lane: 512 / this)
+#endif
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kBufferWord3 = 0x00020000;  // raw buffer: untyped dwords, reads past the end give 0
 
@@ -270,14 +274,13 @@ __global__ __launch_bounds__(NT, 2) void dq_kernel(const BwdArgs a) {
 }
 
 template <int D>
-__global__ __launch_bounds__(NT, 1) void dkdv_kernel(const BwdArgs a) {
+__global__ __launch_bounds__(NT, RA_DKDV_WG_PER_CU) void dkdv_kernel(const BwdArgs a) {
   using L = Lay<D>;
-  // Two stages of the streamed query tile (Q, dO, LSE, Delta): the copies of the next tile run
-  // while the current one is in the matrix cores.
-  __shared__ __attribute__((aligned(1024))) __bf16 q_l[2][L::ELEMS];
-  __shared__ __attribute__((aligned(1024))) __bf16 o_l[2][L::ELEMS];  // the dO tile
-  __shared__ __attribute__((aligned(256))) float lse_l[2][BT];
-  __shared__ __attribute__((aligned(256))) float dlt_l[2][BT];
+  __shared__ __attribute__((aligned(1024))) __bf16 v_l[KT * D];       // V of the workgroup's keys
+  __shared__ __attribute__((aligned(1024))) __bf16 q_l[L::ELEMS];
+  __shared__ __attribute__((aligned(1024))) __bf16 o_l[L::ELEMS];     // the dO tile
+  __shared__ __attribute__((aligned(256))) float lse_l[BT];
+  __shared__ __attribute__((aligned(256))) float dlt_l[BT];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -295,16 +298,22 @@ __global__ __launch_bounds__(NT, 1) void dkdv_kernel(const BwdArgs a) {
   const bool wave_live = wk0 < a.Sk;
   const int rk = min(key, a.Sk - 1);
   const int64_t rs = (int64_t)a.H * D, rs_kv = (int64_t)a.Hkv * D;
-  const uint32_t rowb_q = (uint32_t)rs * 2;
+  const uint32_t rowb_q = (uint32_t)rs * 2, rowb_kv = (uint32_t)rs_kv * 2;
   const float sl2 = a.scale * kLog2e;
 
-  bf16x8 kreg[D / 16], vreg[D / 16];
+  // K of this lane's key in registers (B operand of S = Q K^T); V of the workgroup's KT keys in
+  // LDS (B operand of dP = dO V^T, read per use), laid out as two consecutive swizzled tiles.
+  bf16x8 kreg[D / 16];
   {
     const int64_t off = ((int64_t)b * a.Sk + rk) * rs_kv + (int64_t)hk * D + hh * 8;
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
-      kreg[ks] = *(const bf16x8*)((const __bf16*)a.k[s] + off + ks * 16);
-      vreg[ks] = *(const bf16x8*)((const __bf16*)a.v[s] + off + ks * 16);
+    for (int ks = 0; ks < D / 16; ++ks) kreg[ks] = *(const bf16x8*)((const __bf16*)a.k[s] + off + ks * 16);
+    const char* vbase = (const char*)a.v[s] + ((int64_t)b * a.Sk * rs_kv + (int64_t)hk * D) * 2;
+#pragma unroll
+    for (int half = 0; half < KT / BT; ++half) {
+      const int r0 = k0 + half * BT;
+      const int rows = max(0, min(BT, a.Sk - r0));
+      copy_tile<D>(rows_rsrc(vbase + (int64_t)r0 * rowb_kv, rows, rowb_kv), v_l + half * L::ELEMS, rowb_kv, wave, lane);
     }
   }
   // Queries see a key iff their position is at least the key's: a suffix of the Q share.
@@ -324,43 +333,27 @@ __global__ __launch_bounds__(NT, 1) void dkdv_kernel(const BwdArgs a) {
     for (int r = 0; r < 16; ++r) dk[db][r] = 0.f, dv[db][r] = 0.f;
   const Offsets<D> of(lane);
 
-  // Copies of query tile qt of query head g (of the KV head's group) into stage st: Q and dO
-  // rows by 16-byte LDS DMA over all waves; LSE (natural log) and Delta by 4-byte LDS DMA, one
-  // wave each (lane l lands at word l; rows past the end of the share read as zeros).
-  auto fetch = [&](int g, int qt, int st) {
+  for (int g = 0; g < group; ++g) {
     const int h = hk * group + g;
-    const int q0 = qt * BT;
-    const int rows = min(BT, a.Sq - q0);
     const char* qbase = (const char*)a.q + ((int64_t)b * a.Sq * rs + (int64_t)h * D) * 2;
     const char* obase = (const char*)a.dout + ((int64_t)b * a.Sq * rs + (int64_t)h * D) * 2;
-    copy_tile<D>(rows_rsrc(qbase + (int64_t)q0 * rowb_q, rows, rowb_q), q_l[st], rowb_q, wave, lane);
-    copy_tile<D>(rows_rsrc(obase + (int64_t)q0 * rowb_q, rows, rowb_q), o_l[st], rowb_q, wave, lane);
-    const int64_t srow0 = ((int64_t)b * a.H + h) * a.Sq + q0;
-    if (wave < 2) {
-      const float* src = wave == 0 ? a.lse + srow0 : a.delta + srow0;
-      float* dst = wave == 0 ? lse_l[st] : dlt_l[st];
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rows_rsrc((const char*)src, rows, 4),
-                                               (__attribute__((address_space(3))) void*)dst, 4,
-                                               (uint32_t)lane * 4, 0, 0, 0);
-    }
-  };
-
-  const int n_tiles = n_qt - qt0;  // query tiles per query head (all heads of a group alike)
-  if (n_tiles > 0) {
-    fetch(0, qt0, 0);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-  }
-  int st = 0;
-  for (int g = 0; g < group && n_tiles > 0; ++g) {
+    const int64_t srow0 = ((int64_t)b * a.H + h) * a.Sq;
     for (int qt = qt0; qt < n_qt; ++qt) {
-      // Stage st^1 was last read before the previous barrier: refill it with the next tile.
-      const bool last_of_head = qt + 1 == n_qt;
-      if (!last_of_head || g + 1 < group) fetch(last_of_head ? g + 1 : g, last_of_head ? qt0 : qt + 1, st ^ 1);
       const int q0 = qt * BT;
+      const int rows = min(BT, a.Sq - q0);
+      // Q and dO rows by 16-byte LDS DMA over all waves; LSE (natural log) and Delta by 4-byte
+      // LDS DMA, one wave each (lane l lands at word l; rows past the share's end read as 0).
+      copy_tile<D>(rows_rsrc(qbase + (int64_t)q0 * rowb_q, rows, rowb_q), q_l, rowb_q, wave, lane);
+      copy_tile<D>(rows_rsrc(obase + (int64_t)q0 * rowb_q, rows, rowb_q), o_l, rowb_q, wave, lane);
+      if (wave < 2) {
+        const float* src = (wave == 0 ? a.lse : a.delta) + srow0 + q0;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rows_rsrc((const char*)src, rows, 4),
+                                                 (__attribute__((address_space(3))) void*)(wave == 0 ? lse_l : dlt_l),
+                                                 4, (uint32_t)lane * 4, 0, 0, 0);
+      }
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
       if (wave_live) {
-        const __bf16* qt_l = q_l[st];
-        const __bf16* ot_l = o_l[st];
         const bool masked = q0 + BT > a.Sq || (a.causal && q0 < w_qfirst_max);
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {  // 32 queries at a time
@@ -369,40 +362,41 @@ __global__ __launch_bounds__(NT, 1) void dkdv_kernel(const BwdArgs a) {
           for (int r = 0; r < 16; ++r) sc[r] = 0.f, dp[r] = 0.f;
 #pragma unroll
           for (int ks = 0; ks < D / 16; ++ks) {
-            sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_r<D>(qt_l, of, ks, qb * 32), kreg[ks], sc, 0, 0, 0);
-            dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_r<D>(ot_l, of, ks, qb * 32), vreg[ks], dp, 0, 0, 0);
+            sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_r<D>(q_l, of, ks, qb * 32), kreg[ks], sc, 0, 0, 0);
+            dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_r<D>(o_l, of, ks, qb * 32),
+                                                         read_r<D>(v_l, of, ks, wave * 32), dp, 0, 0, 0);
           }
           // register r of lane l holds query qb*32 + 8*(r/4) + 4*(l/32) + r%4 and key l%32
-          f32x4 ls[4], dl[4];
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            ls[j] = *(const f32x4*)(lse_l[st] + qb * 32 + 8 * j + 4 * hh);
-            dl[j] = *(const f32x4*)(dlt_l[st] + qb * 32 + 8 * j + 4 * hh);
-          }
           bf16x8 pb[2], dsb[2];
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int iq = q0 + qb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);  // local query index
-            const bool vis = !masked || (iq < a.Sq && (!a.causal || iq >= qfirst));
-            const float p = vis ? __builtin_amdgcn_exp2f(fmaf(sc[r], sl2, -ls[r >> 2][r & 3] * kLog2e)) : 0.f;
-            pb[r >> 3][r & 7] = (__bf16)p;
-            dsb[r >> 3][r & 7] = (__bf16)(p * (dp[r] - dl[r >> 2][r & 3]));
+          for (int j = 0; j < 4; ++j) {
+            const f32x4 ls = *(const f32x4*)(lse_l + qb * 32 + 8 * j + 4 * hh);
+            const f32x4 dl = *(const f32x4*)(dlt_l + qb * 32 + 8 * j + 4 * hh);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int r = 4 * j + e;
+              const int iq = q0 + qb * 32 + 8 * j + 4 * hh + e;  // local query index
+              const bool vis = !masked || (iq < a.Sq && (!a.causal || iq >= qfirst));
+              const float p = vis ? __builtin_amdgcn_exp2f(fmaf(sc[r], sl2, -ls[e] * kLog2e)) : 0.f;
+              pb[r >> 3][r & 7] = (__bf16)p;
+              dsb[r >> 3][r & 7] = (__bf16)(p * (dp[r] - dl[e]));
+            }
           }
           // dV^T += dO^T P and dK^T += Q^T dS, 16 queries per MFMA
 #pragma unroll
           for (int c = 0; c < 2; ++c)
 #pragma unroll
             for (int db = 0; db < D / 32; ++db) {
-              dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_t<D>(ot_l, of, db, qb * 32 + c * 16), pb[c], dv[db], 0, 0, 0);
-              dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_t<D>(qt_l, of, db, qb * 32 + c * 16), dsb[c], dk[db], 0, 0, 0);
+              dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_t<D>(o_l, of, db, qb * 32 + c * 16), pb[c], dv[db], 0, 0, 0);
+              dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_t<D>(q_l, of, db, qb * 32 + c * 16), dsb[c], dk[db], 0, 0, 0);
             }
         }
       }
-      __builtin_amdgcn_s_waitcnt(0);  // this wave's copies of the next tile have landed
-      __syncthreads();                // ... and every wave is done with this one
-      st ^= 1;
+      __syncthreads();  // every wave is done with this tile before the next copy
     }
   }
+  // A workgroup whose keys no query sees ran no tile: let its V copies land before it exits.
+  __builtin_amdgcn_s_waitcnt(0);
 
   if (key < a.Sk) {
     const int64_t out = (((int64_t)b * a.Sk + key) * a.Hkv + hk) * D;
