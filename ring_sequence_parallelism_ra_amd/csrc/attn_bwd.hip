@@ -17,7 +17,8 @@
 //                   v_mfma_f32_32x32x16_bf16 (lane = query row), P^T and dS^T in registers,
 //                   and dQ^T += K^T dS^T with K read transposed (ds_read_b64_tr_b16);
 //  * dkdv_kernel    key-stationary: a workgroup owns 128 keys of one (batch, KV head, share)
-//                   with K and V in registers, and walks the query tiles that can see them
+//                   with K in registers and V in LDS (255 registers per lane, so two
+//                   workgroups share a CU), and walks the query tiles that can see them
 //                   for every query head of the KV head's group; per 64-query tile
 //                   S = Q K^T and dP = dO V^T (lane = key), then dV^T += dO^T P and
 //                   dK^T += Q^T dS with Q and dO read transposed. No atomics: each workgroup
