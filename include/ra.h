@@ -24,12 +24,6 @@
  *     as long as they do not write the same memory.
  *   - Device pointers must be 16-byte aligned (128-bit loads and stores).
  *   - Empty inputs (B, H or a sequence length of 0) are valid and launch nothing.
- *   - Environment: RA_PAIR_TILES selects how the bf16 causal attention kernel assigns
- *     query tiles to workgroups: unset or "auto" pairs query tiles n-1-p and p in one
- *     workgroup for striped K/V shares when that still gives at least two workgroups
- *     per compute unit, "always" pairs whenever there are two tiles, "never" keeps one
- *     tile per workgroup. Results agree to rounding either way (the order in which key
- *     tiles are folded differs); read at every launch.
  */
 #ifndef RA_H_
 #define RA_H_

@@ -31,18 +31,13 @@
 //  * Tiles whose keys are all invisible to the workgroup's rows are never visited: the
 //    visible keys of a share form a prefix (positions increase along a share), whose length
 //    comes from the position rule. Only tiles straddling the causal boundary or the ragged
-//    tail evaluate the mask. Workgroups are launched heaviest query tile first; on striped
-//    shares (whose query tiles' work spans 1x to n_qt x) a workgroup instead takes the pair of
-//    query tiles n_qt-1-p and p, the second walked backward, so that every workgroup has the
-//    same work and the resident ones read the same key tiles at the same time.
+//    tail evaluate the mask. Workgroups are launched heaviest query tile first.
 //  * The softmax runs in the log2 domain (exp2 of scores pre-multiplied by scale*log2 e), with
 //    the exact running max as reference, so the largest weight so far is exactly 1 in bf16 (this
 //    keeps peaked softmaxes accurate). O and l are rescaled only on tiles where some row's max
 //    grows (a wave-uniform branch, rarely taken once the first tiles have been seen). LSE is
 //    converted back to the natural log at the end.
 #include <math.h>
-#include <stdlib.h>
-#include <string.h>
 
 #include <type_traits>
 #include <utility>
@@ -81,9 +76,6 @@ constexpr float kLn2 = 0.6931471805599453f;
 #endif
 #ifndef RA_ATTN_TILE_GROUP
 #define RA_ATTN_TILE_GROUP 32         // consecutive tiles of one step visited before the next step
-#endif
-#ifndef RA_ATTN_PAIR
-#define RA_ATTN_PAIR 1                // pair query tiles n_qt-1-p and p in one workgroup (causal, large grids)
 #endif
 #ifndef RA_ATTN_WAVES_PER_SIMD
 #define RA_ATTN_WAVES_PER_SIMD 2      // occupancy target: 256 VGPRs per wave at 2, 512 at 1
@@ -184,6 +176,7 @@ __global__ __launch_bounds__(NT, QB == 1 ? RA_ATTN_WAVES_PER_SIMD : 1) void attn
   const int nbh = a.B * a.H;
   const int n_qt = (a.Sq + BM - 1) / BM;
   const int bh = blockIdx.x % nbh;
+  const int qt = n_qt - 1 - (int)(blockIdx.x / nbh);  // heaviest (latest) query tile first
   const int b = bh / a.H;
   // Consecutive workgroups go to the 8 XCDs in turn, so head (bh mod H) runs on XCD
   // (bh mod 8) when 8 divides H. With grouped KV heads the heads are renumbered so that each
@@ -191,35 +184,13 @@ __global__ __launch_bounds__(NT, QB == 1 ? RA_ATTN_WAVES_PER_SIMD : 1) void attn
   // XCD's L2 instead of each XCD reading every KV head.
   const int hr = bh % a.H;
   const int h = (a.Hkv < a.H && a.H % 8 == 0) ? (hr % 8) * (a.H / 8) + hr / 8 : hr;
+  const int q0 = qt * BM;
+  const int w0 = q0 + wave * WR;  // first row of this wave; block qb owns rows w0+32qb ..
+  const bool wave_live = w0 < a.Sq;
   const int64_t rs = (int64_t)a.H * D;       // elements between consecutive Q/O sequence rows
   const int64_t rs_kv = (int64_t)a.Hkv * D;  // ... and K/V rows
   const int hk = h / (a.H / a.Hkv);          // the KV head this query head reads (GQA/MQA)
   const float sl2 = a.scale * kLog2e;
-
-  // Query tiles of this workgroup. Under a causal mask a query tile's work grows linearly with
-  // its index (for every token assignment), so with a.pair set the workgroup takes the pair
-  // (n_qt-1-p, p), whose work adds up to the same total for every p: the workgroups resident
-  // at once start and end together. The first tile walks its (step, tile) sequence forward and
-  // the second one backward; since the sums are equal, all resident workgroups then read the
-  // same K/V tiles at the same time in both halves, which keeps them sharing L2. Without a.pair
-  // one tile per workgroup, heaviest (latest) first.
-  int qts[2], nparts = 1;
-  if (a.pair) {
-    const int pidx = (int)(blockIdx.x / nbh);
-    qts[0] = n_qt - 1 - pidx;
-    qts[1] = pidx;
-    nparts = pidx < n_qt - 1 - pidx ? 2 : 1;
-  } else {
-    qts[0] = n_qt - 1 - (int)(blockIdx.x / nbh);
-    qts[1] = qts[0];
-  }
-  for (int part = 0; part < nparts; ++part) {
-  const bool rev = part == 1;
-  if (part) __syncthreads();  // the previous tile's LDS stages are free again
-  const int qt = qts[part];
-  const int q0 = qt * BM;
-  const int w0 = q0 + wave * WR;  // first row of this wave; block qb owns rows w0+32qb ..
-  const bool wave_live = w0 < a.Sq;
   auto row_of = [&](int qb) { return w0 + 32 * qb + l32; };
 
   // ---- Q rows of this wave as B operands (k = head dim), resident for the whole kernel.
@@ -340,49 +311,11 @@ __global__ __launch_bounds__(NT, QB == 1 ? RA_ATTN_WAVES_PER_SIMD : 1) void attn
     if (next_g) set_step(c, __builtin_ctzll(next_g), g0 + TG);
   };
 
-  // The inverse of advance: the previous tile of the same sequence; at its start the cursor
-  // stays on the first tile.
-  auto retreat = [&](Cursor& c) {
-    const int g0 = c.t / TG * TG;
-    if (c.t > g0) {  // inside a group of TG tiles of one step
-      --c.t;
-      return;
-    }
-    const uint64_t earlier = c.s <= 0 ? 0ull : (c.s >= 64 ? ~0ull : ((1ull << c.s) - 1));
-    const uint64_t same_g = __builtin_amdgcn_ballot_w64(st_nt > g0) & earlier;
-    if (same_g) {  // the last tile of this group in the latest earlier step that has one
-      const int sp = 63 - __builtin_clzll(same_g);
-      set_step(c, sp, min(g0 + TG, __builtin_amdgcn_readlane(st_nt, sp)) - 1);
-      return;
-    }
-    if (g0 == 0) return;
-    const uint64_t prev_g = __builtin_amdgcn_ballot_w64(st_nt > g0 - TG);
-    if (prev_g) {  // the last tile of the previous group in the last step that has one
-      const int sp = 63 - __builtin_clzll(prev_g);
-      set_step(c, sp, min(g0, __builtin_amdgcn_readlane(st_nt, sp)) - 1);
-    }
-  };
-  auto move = [&](Cursor& c) {
-    if (rev) retreat(c);
-    else advance(c);
-  };
-
-  int total = 0, max_nt = 0;
-  for (int s = 0; s < a.nsteps; ++s) {
-    const int n = __builtin_amdgcn_readlane(st_nt, s);
-    total += n;
-    max_nt = max(max_nt, n);
-  }
+  int total = 0;
+  for (int s = 0; s < a.nsteps; ++s) total += __builtin_amdgcn_readlane(st_nt, s);
   Cursor cur = {-1, 0, 0, 0, 0, nullptr, nullptr};
-  if (total > 0) {
-    if (!rev) {
-      set_step(cur, __builtin_ctzll(__builtin_amdgcn_ballot_w64(st_nt > 0)), 0);
-    } else {  // the last tile of the forward sequence: last group, last step that has tiles in it
-      const int g_last = (max_nt - 1) / TG * TG;
-      const int sp = 63 - __builtin_clzll(__builtin_amdgcn_ballot_w64(st_nt > g_last));
-      set_step(cur, sp, min(g_last + TG, __builtin_amdgcn_readlane(st_nt, sp)) - 1);
-    }
-  }
+  const uint64_t first = __builtin_amdgcn_ballot_w64(st_nt > 0);
+  if (first) set_step(cur, __builtin_ctzll(first), 0);
 
   if (total > 0) {
     // Copy one tile of K or V from HBM into an LDS tile. Lane `lane` of copy i of wave w fills
@@ -573,9 +506,9 @@ __global__ __launch_bounds__(NT, QB == 1 ? RA_ATTN_WAVES_PER_SIMD : 1) void attn
 
     // Prologue: K and V of tile 0 and K of tile 1 resident.
     Cursor nx = cur;
-    move(nx);
+    advance(nx);
     Cursor k2 = nx;
-    move(k2);
+    advance(k2);
     dma(tile_rsrc(cur.kb, cur.t), k_lds0, true);
     dma(tile_rsrc(cur.vb, cur.t), v_lds0, false);
     dma(tile_rsrc(nx.kb, nx.t), k_lds1, true);
@@ -607,7 +540,7 @@ __global__ __launch_bounds__(NT, QB == 1 ? RA_ATTN_WAVES_PER_SIMD : 1) void attn
       __syncthreads();
       cur = nx;
       nx = k2;
-      move(k2);
+      advance(k2);
     };
     for (int j = 0; j < total; j += 2) {
       iteration(std::integral_constant<int, 0>(), s0, s1);
@@ -650,46 +583,13 @@ __global__ __launch_bounds__(NT, QB == 1 ? RA_ATTN_WAVES_PER_SIMD : 1) void attn
       }
     }
   }
-  }  // part
 }
 
 }  // namespace
 
-// Compute units of the current device (cached per device).
-static int device_cus() {
-  static int cache[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  if (cache[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-    cache[dev] = n;
-  }
-  return cache[dev];
-}
-
-// RA_PAIR_TILES override of the automatic pairing choice: 1 "always", -1 "never", 0 automatic.
-static int pair_override() {
-  const char* e = getenv("RA_PAIR_TILES");
-  if (!e) return 0;
-  if (!strcmp(e, "always")) return 1;
-  if (!strcmp(e, "never")) return -1;
-  return 0;
-}
-
-hipError_t launch_attn_bf16(const AttnArgs& args, int D, int o_dtype, hipStream_t stream) {
-  AttnArgs a = args;
+hipError_t launch_attn_bf16(const AttnArgs& a, int D, int o_dtype, hipStream_t stream) {
   const int n_qt = (a.Sq + BM - 1) / BM;
-  // Pair query tiles (see the kernel) on striped K/V shares when the halved grid still fills
-  // every CU twice. Measured same-box A/B: striped shares gain (their query tiles' work spans
-  // 1x to n_qt x, and unpaired the late-starting workgroups miss in L2: 45% hit rate against
-  // 88% for zigzag), +2.6% at 256K tokens over 8 ranks and +0.6% at 32K; contiguous and zigzag
-  // shares, whose resident workgroups already walk in step, lose about 2%.
-  const int64_t pairs = (int64_t)(n_qt + 1) / 2 * a.B * a.H;
-  const int mode = pair_override();
-  const bool automatic = a.kv_assign == RA_STRIPED && pairs >= 2 * (int64_t)device_cus();
-  a.pair = RA_ATTN_PAIR && a.causal && n_qt >= 2 && (mode > 0 || (mode == 0 && automatic));
-  const int64_t grid = a.pair ? pairs : (int64_t)n_qt * a.B * a.H;
+  const int64_t grid = (int64_t)n_qt * a.B * a.H;
   if (grid == 0) return hipSuccess;
   dim3 g((unsigned)grid), blk(NT);
   if (D == 128) {

@@ -86,7 +86,6 @@ struct AttnArgs {
   int32_t causal;
   int32_t load_state;
   int32_t store_final;  // 1: write normalised O and LSE; 0: write the running state
-  int32_t pair;         // bf16 kernel: set by its launcher (two query tiles per workgroup)
   Pos qpos;             // rule for Q rows
   int32_t kv_assign, kv_world;
   int64_t kv_len;       // global length of the KV rule (rank comes from kv_rank[s])
