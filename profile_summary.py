@@ -9,8 +9,8 @@
            in turn, the last label taking every later run.
   traffic  HBM bytes per launch of one kernel from two ``--pmc`` runs (FETCH_SIZE, then
            WRITE_SIZE, KiB per dispatch), each scaled by what the same counter reads for a
-           plain copy kernel of known size run in the same process (the Ulysses permute:
-           every call reads and writes the same known number of bytes). Writes the JSON
+           plain copy kernel of known size run in the same process (the HIP runtime's copy
+           kernel behind the bench's 64 MiB device-to-device copy; median over its dispatches). Writes the JSON
            that bench.py reports as ``roofline.traffic`` (only while the kernel source hash
            still matches). ``--first N`` keeps the kernel's first N dispatches only (the
            headline runs first in bench.py; later workloads may share its grid size).
@@ -71,7 +71,7 @@ def trace(args):
     print(text)
 
 
-def _counter(path, kernel, grid, name, first=0):
+def _counter(path, kernel, grid, name, first=0, median=False):
     rows = [r for r in csv.DictReader(open(path))
             if _short(r["Kernel_Name"]).startswith(kernel) and int(r["Grid_Size"]) == grid
             and r["Counter_Name"] == name]
@@ -79,14 +79,15 @@ def _counter(path, kernel, grid, name, first=0):
     vals = [float(r["Counter_Value"]) for r in rows][: first or None]
     if not vals:
         raise SystemExit(f"no {name} samples for {kernel} grid {grid} in {path}")
-    return statistics.mean(vals), len(vals)
+    return (statistics.median(vals) if median else statistics.mean(vals)), len(vals)
 
 
 def traffic(args):
     f_k, nf = _counter(args.fetch, args.kernel, args.grid, "FETCH_SIZE", args.first)
     w_k, nw = _counter(args.write, args.kernel, args.grid, "WRITE_SIZE", args.first)
-    f_c, _ = _counter(args.fetch, args.calib_kernel, args.calib_grid, "FETCH_SIZE")
-    w_c, _ = _counter(args.write, args.calib_kernel, args.calib_grid, "WRITE_SIZE")
+    # median: a runtime copy kernel of this grid may also serve other copies
+    f_c, _ = _counter(args.fetch, args.calib_kernel, args.calib_grid, "FETCH_SIZE", median=True)
+    w_c, _ = _counter(args.write, args.calib_kernel, args.calib_grid, "WRITE_SIZE", median=True)
     ff = args.calib_bytes / (f_c * 1024.0)
     fw = args.calib_bytes / (w_c * 1024.0)
     fetch_b = f_k * 1024.0 * ff
