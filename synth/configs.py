@@ -10,7 +10,10 @@ mesh (Ulysses degree u = 4 inside a group, zigzag ring of r = 2 groups, 128K tok
 pages' 8-GPU u=4, r=2 run): ``world`` and ``rank`` are the ring degree and ring rank,
 ``ulysses`` and ``ulysses_rank`` the Ulysses degree and the device's head group.
 ``gqa_zigzag_rank3`` is grouped-query attention with the head counts of the pages' GQA example
-(64 query heads sharing 8 KV heads), on a 64K-token zigzag ring of 8.
+(64 query heads sharing 8 KV heads), on a 64K-token zigzag ring of 8. ``contig_rank7_256k`` and
+``striped_rank7_256k`` are the heaviest ranks of the contiguous and striped assignments of the
+headline's sequence (256K tokens over 8 ranks, 16 heads): the shares the pages' Striped Attention
+comparison sets against each other.
 """
 from __future__ import annotations
 
@@ -59,6 +62,10 @@ CONFIGS = {
                          sampled_rows=512, ulysses=4, ulysses_rank=2),
     "gqa_zigzag_rank3": Workload("gqa_zigzag_rank3", 7, 1, 64, 128, 65536, 8, 3, "zigzag", True, "bf16",
                                  sampled_rows=512, kv_heads=8),
+    "contig_rank7_256k": Workload("contig_rank7_256k", 8, 1, 16, 128, 262144, 8, 7, "contiguous", True, "bf16",
+                                  sampled_rows=512),
+    "striped_rank7_256k": Workload("striped_rank7_256k", 9, 1, 16, 128, 262144, 8, 7, "striped", True, "bf16",
+                                   sampled_rows=512),
 }
 
 

@@ -107,6 +107,13 @@ def test_gqa_zigzag_rank3_sampled():
     _sampled_ring("gqa_zigzag_rank3")
 
 
+@pytest.mark.parametrize("name", ["contig_rank7_256k", "striped_rank7_256k"])
+def test_assignment_comparison_heaviest_ranks_sampled(name):
+    # the heaviest contiguous and striped ranks of the headline's 256K-token, 8-rank sequence,
+    # as the bench's assignment comparison times them (all 8 ring steps in one call)
+    _sampled_ring(name)
+
+
 def test_ulysses_local():
     w = synth.get("ulysses_local")
     gq, gk, gv = synth.global_qkv(w)
