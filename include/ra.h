@@ -24,6 +24,12 @@
  *     as long as they do not write the same memory.
  *   - Device pointers must be 16-byte aligned (128-bit loads and stores).
  *   - Empty inputs (B, H or a sequence length of 0) are valid and launch nothing.
+ *   - Environment: RA_KV_SPLIT selects the workgroup layout of the bf16 attention
+ *     kernel. Unset or "auto": when one workgroup per 128-row query tile would leave a
+ *     compute unit with fewer than two workgroups, each query tile's key tiles are
+ *     split between two groups of waves of one workgroup and their states merged at the
+ *     end; "always" / "never" force either layout. Results agree to rounding (the
+ *     order in which key tiles are folded differs); read at every launch.
  */
 #ifndef RA_H_
 #define RA_H_

@@ -32,12 +32,18 @@
 //    visible keys of a share form a prefix (positions increase along a share), whose length
 //    comes from the position rule. Only tiles straddling the causal boundary or the ragged
 //    tail evaluate the mask. Workgroups are launched heaviest query tile first.
+//  * Short shares (fewer query tiles than two per CU) run a workgroup of two such wave groups
+//    on the same query rows, each folding every other key tile of the sequence into its own
+//    (m, l, O); the two states are merged through LDS at the end with the log-sum-exp update.
+//    That puts two waves on every SIMD where one workgroup per query tile would leave one.
 //  * The softmax runs in the log2 domain (exp2 of scores pre-multiplied by scale*log2 e), with
 //    the exact running max as reference, so the largest weight so far is exactly 1 in bf16 (this
 //    keeps peaked softmaxes accurate). O and l are rescaled only on tiles where some row's max
 //    grows (a wave-uniform branch, rarely taken once the first tiles have been seen). LSE is
 //    converted back to the natural log at the end.
 #include <math.h>
+#include <stdlib.h>
+#include <string.h>
 
 #include <type_traits>
 #include <utility>
@@ -156,19 +162,28 @@ __device__ __forceinline__ void sched_chunk(std::integer_sequence<int, I...>) {
    ...);
 }
 
-template <int D, class Out>
-__global__ __launch_bounds__(NT, QB == 1 ? RA_ATTN_WAVES_PER_SIMD : 1) void attn_bf16_kernel(const AttnArgs a) {
+// KVS = 1: one group of RA_ATTN_WAVES waves visits every K/V tile of the workgroup's sequence.
+// KVS = 2 (grids too small to put two workgroups on every CU): two such groups own the same
+// query rows, group g folding the tiles at odd (g = 1) or even (g = 0) places of the sequence
+// into its own (m, l, O); the groups' states are merged through LDS at the end, like two
+// blocks of the ring merged by the log-sum-exp update. Each SIMD then holds two waves.
+template <int D, class Out, int KVS>
+__global__ __launch_bounds__(NT * KVS, QB == 1 ? RA_ATTN_WAVES_PER_SIMD : 1) void attn_bf16_kernel(const AttnArgs a) {
   using C = Cfg<D>;
+  static_assert(KVS == 1 || (KVS == 2 && QB == 1), "the key split merges one 32-row block per wave");
   // The two stages of K and V are four distinct LDS objects: the copies into one stage and the
   // reads of the other can then be told apart, so no wait for in-flight copies is inserted
   // before the reads.
-  __shared__ __attribute__((aligned(1024))) __bf16 k_lds0[C::ELEMS];
-  __shared__ __attribute__((aligned(1024))) __bf16 k_lds1[C::ELEMS];
-  __shared__ __attribute__((aligned(1024))) __bf16 v_lds0[C::ELEMS];
-  __shared__ __attribute__((aligned(1024))) __bf16 v_lds1[C::ELEMS];
+  __shared__ __attribute__((aligned(1024))) __bf16 k_lds0[C::ELEMS * KVS];
+  __shared__ __attribute__((aligned(1024))) __bf16 k_lds1[C::ELEMS * KVS];
+  __shared__ __attribute__((aligned(1024))) __bf16 v_lds0[C::ELEMS * KVS];
+  __shared__ __attribute__((aligned(1024))) __bf16 v_lds1[C::ELEMS * KVS];
 
   const int tid = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keep in SGPRs
+  const int wave_wg = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keep in SGPRs
+  const int grp = KVS == 1 ? 0 : wave_wg / RA_ATTN_WAVES;        // key-split group
+  const int wave = KVS == 1 ? wave_wg : wave_wg % RA_ATTN_WAVES;  // wave within the group
+  const int goff = grp * C::ELEMS;                                // the group's LDS tiles
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int hh = lane >> 5;
@@ -231,7 +246,7 @@ __global__ __launch_bounds__(NT, QB == 1 ? RA_ATTN_WAVES_PER_SIMD : 1) void attn
 
   auto state_row = [&](int qb) { return ((int64_t)b * a.H + h) * a.Sq + row_of(qb); };    // [B, H, S]
   auto out_row = [&](int qb) { return (((int64_t)b * a.Sq + row_of(qb)) * a.H + h) * D; };  // [B, S, H, D]
-  if (a.load_state) {
+  if (a.load_state && grp == 0) {  // a split workgroup resumes in group 0 only
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       if (row_of(qb) >= a.Sq) continue;
@@ -311,11 +326,21 @@ __global__ __launch_bounds__(NT, QB == 1 ? RA_ATTN_WAVES_PER_SIMD : 1) void attn
     if (next_g) set_step(c, __builtin_ctzll(next_g), g0 + TG);
   };
 
+  // With the key split, each group takes every KVS-th tile of the sequence from its own start.
+  auto step = [&](Cursor& c) {
+    advance(c);
+    if constexpr (KVS == 2) advance(c);
+  };
+
   int total = 0;
   for (int s = 0; s < a.nsteps; ++s) total += __builtin_amdgcn_readlane(st_nt, s);
   Cursor cur = {-1, 0, 0, 0, 0, nullptr, nullptr};
   const uint64_t first = __builtin_amdgcn_ballot_w64(st_nt > 0);
   if (first) set_step(cur, __builtin_ctzll(first), 0);
+  if (KVS == 2 && grp == 1) advance(cur);
+  // iterations of the loop (the same for every wave: barriers) and tiles of this wave's group
+  const int n_iter = KVS == 1 ? total : (total + 1) / 2;
+  const int my_tiles = KVS == 1 ? total : (total + 1 - grp) / 2;
 
   if (total > 0) {
     // Copy one tile of K or V from HBM into an LDS tile. Lane `lane` of copy i of wave w fills
@@ -506,30 +531,30 @@ __global__ __launch_bounds__(NT, QB == 1 ? RA_ATTN_WAVES_PER_SIMD : 1) void attn
 
     // Prologue: K and V of tile 0 and K of tile 1 resident.
     Cursor nx = cur;
-    advance(nx);
+    step(nx);
     Cursor k2 = nx;
-    advance(k2);
-    dma(tile_rsrc(cur.kb, cur.t), k_lds0, true);
-    dma(tile_rsrc(cur.vb, cur.t), v_lds0, false);
-    dma(tile_rsrc(nx.kb, nx.t), k_lds1, true);
+    step(k2);
+    dma(tile_rsrc(cur.kb, cur.t), k_lds0 + goff, true);
+    dma(tile_rsrc(cur.vb, cur.t), v_lds0 + goff, false);
+    dma(tile_rsrc(nx.kb, nx.t), k_lds1 + goff, true);
     __builtin_amdgcn_s_waitcnt(0);  // this wave's copies have landed in LDS
     __syncthreads();
 
     f32x16 s0[QB][BN / 32], s1[QB][BN / 32];
-    if (wave_live) qk(k_lds0, s0);
+    if (wave_live && (KVS == 1 || my_tiles > 0)) qk(k_lds0 + goff, s0);
     __syncthreads();  // every wave has read K(0) before iteration 0 copies K(2) over it
     // Iteration j (stage sl = j mod 2): LDS holds K(j+1) in stage sl^1 and V(j) in stage sl;
     // registers hold the scores of tile j. It loads K(j+2) into stage sl of K and V(j+1) into
     // stage sl^1 of V, computes the scores of tile j+1 and folds tile j in.
-    auto iteration = [&](auto stage, f32x16 (&sc)[QB][BN / 32], f32x16 (&sn)[QB][BN / 32]) {
+    auto iteration = [&](auto stage, int it, f32x16 (&sc)[QB][BN / 32], f32x16 (&sn)[QB][BN / 32]) {
       constexpr int sl = decltype(stage)::value;
-      __bf16* k_fill = sl ? k_lds1 : k_lds0;
-      __bf16* v_fill = sl ? v_lds0 : v_lds1;
-      const __bf16* k_read = sl ? k_lds0 : k_lds1;
-      const __bf16* v_read = sl ? v_lds1 : v_lds0;
+      __bf16* k_fill = (sl ? k_lds1 : k_lds0) + goff;
+      __bf16* v_fill = (sl ? v_lds0 : v_lds1) + goff;
+      const __bf16* k_read = (sl ? k_lds0 : k_lds1) + goff;
+      const __bf16* v_read = (sl ? v_lds1 : v_lds0) + goff;
       dma(tile_rsrc(k2.kb, k2.t), k_fill, true);
       dma(tile_rsrc(nx.vb, nx.t), v_fill, false);
-      if (wave_live) {
+      if (wave_live && (KVS == 1 || it < my_tiles)) {
         float base[QB];
         prepare(cur, sc, base);
         if (RA_ATTN_SETPRIO) __builtin_amdgcn_s_setprio(1);
@@ -540,13 +565,41 @@ __global__ __launch_bounds__(NT, QB == 1 ? RA_ATTN_WAVES_PER_SIMD : 1) void attn
       __syncthreads();
       cur = nx;
       nx = k2;
-      advance(k2);
+      step(k2);
     };
-    for (int j = 0; j < total; j += 2) {
-      iteration(std::integral_constant<int, 0>(), s0, s1);
-      if (j + 1 >= total) break;
-      iteration(std::integral_constant<int, 1>(), s1, s0);
+    for (int j = 0; j < n_iter; j += 2) {
+      iteration(std::integral_constant<int, 0>(), j, s0, s1);
+      if (j + 1 >= n_iter) break;
+      iteration(std::integral_constant<int, 1>(), j + 1, s1, s0);
     }
+  }
+
+  if constexpr (KVS == 2) {
+    // Merge group 1's state into group 0's: wave w of group 1 leaves (m, l, O) in one of the
+    // four stage buffers (lane-contiguous words), wave w of group 0 folds it in with the
+    // log-sum-exp update (a side that has seen no key contributes nothing).
+    float* xs = (float*)(wave == 0 ? k_lds0 : wave == 1 ? k_lds1 : wave == 2 ? v_lds0 : v_lds1);
+    __syncthreads();  // every wave is done with the K/V tiles
+    if (grp == 1) {
+      xs[lane] = m_run[0];
+      xs[64 + lane] = l_run[0];
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) xs[(2 + db * 16 + r) * 64 + lane] = oacc[0][db][r];
+    }
+    __syncthreads();
+    if (grp == 1) return;  // no barrier follows
+    const float mb = xs[lane], lb = xs[64 + lane];
+    const float m = fmaxf(m_run[0], mb);
+    const float fa = m_run[0] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run[0] - m);
+    const float fb = mb == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mb - m);
+    m_run[0] = m;
+    l_run[0] = l_run[0] * fa + lb * fb;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[0][db][r] = oacc[0][db][r] * fa + xs[(2 + db * 16 + r) * 64 + lane] * fb;
   }
 
   // ---- epilogue
@@ -587,18 +640,49 @@ __global__ __launch_bounds__(NT, QB == 1 ? RA_ATTN_WAVES_PER_SIMD : 1) void attn
 
 }  // namespace
 
+// Compute units of the current device (cached per device).
+static int device_cus() {
+  static int cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
+// RA_KV_SPLIT override of the automatic key-split choice: 1 "always", -1 "never", 0 automatic.
+static int kv_split_override() {
+  const char* e = getenv("RA_KV_SPLIT");
+  if (!e) return 0;
+  if (!strcmp(e, "always")) return 1;
+  if (!strcmp(e, "never")) return -1;
+  return 0;
+}
+
+template <int KVS>
+static void launch(const AttnArgs& a, int D, int o_dtype, dim3 g, hipStream_t stream) {
+  dim3 blk(NT * KVS);
+  if (D == 128) {
+    if (o_dtype == RA_BF16) hipLaunchKernelGGL((attn_bf16_kernel<128, OutBf16, KVS>), g, blk, 0, stream, a);
+    else hipLaunchKernelGGL((attn_bf16_kernel<128, OutF32, KVS>), g, blk, 0, stream, a);
+  } else {
+    if (o_dtype == RA_BF16) hipLaunchKernelGGL((attn_bf16_kernel<64, OutBf16, KVS>), g, blk, 0, stream, a);
+    else hipLaunchKernelGGL((attn_bf16_kernel<64, OutF32, KVS>), g, blk, 0, stream, a);
+  }
+}
+
 hipError_t launch_attn_bf16(const AttnArgs& a, int D, int o_dtype, hipStream_t stream) {
   const int n_qt = (a.Sq + BM - 1) / BM;
   const int64_t grid = (int64_t)n_qt * a.B * a.H;
   if (grid == 0) return hipSuccess;
-  dim3 g((unsigned)grid), blk(NT);
-  if (D == 128) {
-    if (o_dtype == RA_BF16) hipLaunchKernelGGL((attn_bf16_kernel<128, OutBf16>), g, blk, 0, stream, a);
-    else hipLaunchKernelGGL((attn_bf16_kernel<128, OutF32>), g, blk, 0, stream, a);
-  } else {
-    if (o_dtype == RA_BF16) hipLaunchKernelGGL((attn_bf16_kernel<64, OutBf16>), g, blk, 0, stream, a);
-    else hipLaunchKernelGGL((attn_bf16_kernel<64, OutF32>), g, blk, 0, stream, a);
-  }
+  // Key split when one workgroup per query tile leaves CUs with fewer than two workgroups.
+  const int mode = kv_split_override();
+  const bool split = QB == 1 && (mode > 0 || (mode == 0 && grid < 2 * (int64_t)device_cus()));
+  if (split) launch<2>(a, D, o_dtype, dim3((unsigned)grid), stream);
+  else launch<1>(a, D, o_dtype, dim3((unsigned)grid), stream);
   return hipGetLastError();
 }
 
