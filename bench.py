@@ -431,7 +431,7 @@ def main():
     achieved = head["flops"] / (head["kernel_ms_mean"] * 1e-3) / 1e12
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic_for(head["kernel_ms_mean"]),
-                "kernel": "attn_bf16_kernel<128, OutBf16>", "kernel_ms": round(head["kernel_ms_mean"], 4),
+                "kernel": "attn_bf16_kernel<128, OutBf16, 1>", "kernel_ms": round(head["kernel_ms_mean"], 4),
                 "flops_per_launch": head["flops"]}
 
     secondary = {}
