@@ -680,9 +680,13 @@ hipError_t launch_attn_bf16(const AttnArgs& a, int D, int o_dtype, hipStream_t s
   if (grid == 0) return hipSuccess;
   // Key split when one workgroup per query tile leaves CUs with fewer than two workgroups.
   const int mode = kv_split_override();
-  const bool split = QB == 1 && (mode > 0 || (mode == 0 && grid < 2 * (int64_t)device_cus()));
-  if (split) launch<2>(a, D, o_dtype, dim3((unsigned)grid), stream);
-  else launch<1>(a, D, o_dtype, dim3((unsigned)grid), stream);
+  if constexpr (QB == 1) {  // the split layout merges one 32-row block per wave
+    if (mode > 0 || (mode == 0 && grid < 2 * (int64_t)device_cus())) {
+      launch<2>(a, D, o_dtype, dim3((unsigned)grid), stream);
+      return hipGetLastError();
+    }
+  }
+  launch<1>(a, D, o_dtype, dim3((unsigned)grid), stream);
   return hipGetLastError();
 }
 
