@@ -8,12 +8,13 @@ workload -- B=1, H=16, D=128, L=262144 over N=8 ranks in 16 chunks of 16384, ran
 causal-adjusted TFLOP/s: 4*D FLOPs per visible (query, key) pair per head, the pairs counted
 by the library's planner from the same position rule the kernel uses.
 
-Also reported in the same JSON line (``secondary``): the other bf16 workloads (contiguous
+Also reported in the same JSON line (``secondary``): the other workloads (contiguous
 rank 7 of L=8192, striped rank 0 of L=32768 at std 1 and 4, grouped-query attention with 64
 query heads on 8 KV heads on a zigzag ring of L=65536, the Ulysses local step of
 L=65536 with its permutes, one device of a 128K-token USP mesh with Ulysses degree 4 and a
 zigzag ring of 2, the backward pass of the headline share, the heaviest rank of each token
-assignment at the pages' Striped Attention sizes), the LSE-merge bandwidth, the
+assignment at the pages' Striped Attention sizes, the tiny exact fp32 ring), the LSE-merge
+bandwidth, the
 roofline of the attention kernel and the oracle timed on the host cores (``cpu_baseline``).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-secondary | --secondary a,b,...]
@@ -318,6 +319,34 @@ def bench_balance(steps, warmup):
     return out
 
 
+def bench_tiny(steps, warmup):
+    """The tiny exact fp32 workload (B1 H1 L256 D64, 4 contiguous ranks, non-causal): one
+    ra_ring_share per rank, each 4 ring steps of 64 keys. Reported for completeness, not held to
+    the matrix-core roofline: the fp32 path gives every query row one lane and computes logits,
+    maximum and sum in fp64 on the vector ALUs, so a 64-query share is a single wave and its
+    time is that wave's latency through 256 keys (a few hundred microseconds)."""
+    import torch
+
+    import ring_sequence_parallelism_ra_amd as ra
+    import synth
+    w = synth.get("tiny_exact")
+    gq, gk, gv = (torch.from_numpy(x).cuda() for x in synth.global_qkv(w))
+    n, L = w.world, w.global_len
+    pos = [ra.debug_positions(ra.Shard(w.assign, n, r, L)) for r in range(n)]
+    ks = [torch.index_select(gk, 1, p).contiguous() for p in pos]
+    vs = [torch.index_select(gv, 1, p).contiguous() for p in pos]
+    calls = [ra.prepare_ring_share(torch.index_select(gq, 1, pos[r]).contiguous(), ks, vs, r, assign=w.assign,
+                                   causal=False)[0] for r in range(n)]
+
+    def all_ranks():
+        for c in calls:
+            c()
+
+    _, ev, _ = time_calls(all_ranks, steps, warmup, SETTLE_S)
+    flops = 4 * w.head_dim * w.heads * w.batch * L * L  # every rank's 64 queries against all 256 keys
+    return {"us_per_rank_call": 1e3 * ev / n, "tflops": flops / (ev * 1e-3) / 1e12, "dtype": "f32"}
+
+
 def bench_merge(steps, warmup):
     import torch
 
@@ -409,7 +438,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     args = ap.parse_args()
     every = ("contig_rank7", "striped_rank0", "striped_rank0_std4", "gqa_zigzag_rank3", "ulysses_local", "usp_u4r2",
-             "backward_zigzag_rank3", "lse_merge", "striped_vs_contiguous")
+             "backward_zigzag_rank3", "lse_merge", "striped_vs_contiguous", "tiny_exact")
     chosen = () if args.no_secondary else (tuple(args.secondary.split(",")) if args.secondary else every)
     unknown = [c for c in chosen if c not in every]
     if unknown:
@@ -463,6 +492,10 @@ def main():
                     log(f"[bench] striped_vs_contiguous {k}: heaviest-rank share contiguous {v['contiguous']['ms']:.1f} ms, "
                         f"striped {v['striped']['ms']:.1f} ms, zigzag {v['zigzag']['ms']:.1f} ms -> striped "
                         f"{v['striped_speedup']}x, zigzag {v['zigzag_speedup']}x over contiguous")
+        if "tiny_exact" in chosen:
+            t = bench_tiny(args.steps, args.warmup)
+            secondary["tiny_exact"] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in t.items()}
+            log(f"[bench] tiny_exact: {t['us_per_rank_call']:.1f} us per rank's ring call (fp32, one wave per share)")
         if "lse_merge" in chosen:
             m = bench_merge(args.steps, args.warmup)
             secondary["lse_merge"] = {k: (round(v, 3) if isinstance(v, float) else v) for k, v in m.items()}
