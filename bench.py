@@ -40,7 +40,8 @@ PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 FL
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 HEADLINE = "zigzag_rank3"
 SETTLE_S = 0.3              # warm-up and minimum timed span of the short secondary workloads
-KERNEL_SRC = os.path.join(ROOT, "ring_sequence_parallelism_ra_amd", "csrc", "attn_bf16.hip")
+KERNEL_SRC = [os.path.join(ROOT, "ring_sequence_parallelism_ra_amd", "csrc", f)
+              for f in ("attn_bf16.hip", "attn_bf16_tile.inc")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_bf16_zigzag_rank3_traffic.json")
 
 
@@ -49,8 +50,11 @@ def log(*a):
 
 
 def kernel_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in KERNEL_SRC:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def to_dev(bits):
@@ -460,7 +464,7 @@ def main():
     achieved = head["flops"] / (head["kernel_ms_mean"] * 1e-3) / 1e12
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic_for(head["kernel_ms_mean"]),
-                "kernel": "attn_bf16_kernel<128, OutBf16, 1>", "kernel_ms": round(head["kernel_ms_mean"], 4),
+                "kernel": "attn_bf16_kernel<128, OutBf16, 1, 0>", "kernel_ms": round(head["kernel_ms_mean"], 4),
                 "flops_per_launch": head["flops"]}
 
     secondary = {}

@@ -30,6 +30,12 @@
  *     split between two groups of waves of one workgroup and their states merged at the
  *     end; "always" / "never" force either layout. Results agree to rounding (the
  *     order in which key tiles are folded differs); read at every launch.
+ *   - Environment: RA_PAIR_TILES. Unset or "auto": for causal calls on striped K/V
+ *     shares whose grid still gives two workgroups per compute unit when halved, one
+ *     workgroup takes the query tiles n-1-p and p (the second walked backward over its
+ *     key tiles); "always" pairs every causal call with two or more query tiles (unless
+ *     the key split applies), "never" keeps one tile per workgroup. Results agree to
+ *     rounding either way; read at every launch.
  */
 #ifndef RA_H_
 #define RA_H_

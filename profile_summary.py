@@ -92,7 +92,10 @@ def traffic(args):
     fw = args.calib_bytes / (w_c * 1024.0)
     fetch_b = f_k * 1024.0 * ff
     write_b = w_k * 1024.0 * fw
-    src_hash = hashlib.sha256(open(args.src, "rb").read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in args.src:  # the kernel's source files, in the order bench.py hashes them
+        h.update(open(path, "rb").read())
+    src_hash = h.hexdigest()[:16]
     out = {"kernel": args.kernel, "grid": args.grid, "bytes_per_launch": round(fetch_b + write_b),
            "fetch_bytes": round(fetch_b), "write_bytes": round(write_b),
            "fetch_kib_raw": f_k, "write_kib_raw": w_k, "launches": [nf, nw],
@@ -252,7 +255,7 @@ def main():
     w.add_argument("--calib-kernel", required=True)
     w.add_argument("--calib-grid", type=int, required=True)
     w.add_argument("--calib-bytes", type=int, required=True)
-    w.add_argument("--src", required=True)
+    w.add_argument("--src", action="append", required=True)
     w.add_argument("--cmd", required=True)
     w.add_argument("--out", required=True)
     p = sub.add_parser("pmc")
