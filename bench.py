@@ -327,8 +327,9 @@ def bench_tiny(steps, warmup):
     """The tiny exact fp32 workload (B1 H1 L256 D64, 4 contiguous ranks, non-causal): one
     ra_ring_share per rank, each 4 ring steps of 64 keys. Reported for completeness, not held to
     the matrix-core roofline: the fp32 path gives every query row one lane and computes logits,
-    maximum and sum in fp64 on the vector ALUs, so a 64-query share is a single wave and its
-    time is that wave's latency through 256 keys (a few hundred microseconds)."""
+    maximum and sum in fp64 on the vector ALUs; a 64-query share is one workgroup whose four
+    waves fold a quarter of the keys each, so its time is the latency of 64 keys' fp64 work per
+    lane plus the merge (about a hundred microseconds)."""
     import torch
 
     import ring_sequence_parallelism_ra_amd as ra
@@ -499,7 +500,7 @@ def main():
         if "tiny_exact" in chosen:
             t = bench_tiny(args.steps, args.warmup)
             secondary["tiny_exact"] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in t.items()}
-            log(f"[bench] tiny_exact: {t['us_per_rank_call']:.1f} us per rank's ring call (fp32, one wave per share)")
+            log(f"[bench] tiny_exact: {t['us_per_rank_call']:.1f} us per rank's ring call (fp32, latency-bound)")
         if "lse_merge" in chosen:
             m = bench_merge(args.steps, args.warmup)
             secondary["lse_merge"] = {k: (round(v, 3) if isinstance(v, float) else v) for k, v in m.items()}

@@ -1,11 +1,12 @@
-"""GPU parity of both workgroup layouts of the bf16 attention kernel.
+"""GPU parity of both workgroup layouts of the attention kernels (bf16 and fp32).
 
 When one workgroup per query tile would leave a CU with fewer than two workgroups, the launcher
 splits each query tile's key tiles between two groups of waves in one workgroup (even and odd
 places of the tile sequence) and merges their states through LDS at the end. The small parity
 cases of test_gpu_kernels therefore run the split layout by default; here they run again with
 RA_KV_SPLIT=never (the layout every large workload uses), and a large share runs with the
-split forced, against the oracle and against the unsplit result.
+split forced, against the oracle and against the unsplit result. The fp32 kernel splits small
+grids the same way (four waves on one 64-row query tile, merged in fp64).
 """
 import numpy as np
 import pytest
@@ -33,14 +34,16 @@ def never_split(monkeypatch):
 @pytest.mark.usefixtures("never_split")
 @pytest.mark.parametrize("case", K.RING_CASES, ids=[f"{a}-N{n}-L{l}" for a, n, l in K.RING_CASES])
 @pytest.mark.parametrize("causal", [True, False])
-def test_ring_share_parity_unsplit(case, causal):
-    K.test_ring_share_parity(case, "bf16", causal)
+@pytest.mark.parametrize("in_dt", ["bf16", "f32"])
+def test_ring_share_parity_unsplit(case, causal, in_dt):
+    K.test_ring_share_parity(case, in_dt, causal)
 
 
 @pytest.mark.usefixtures("never_split")
 @pytest.mark.parametrize("assign", K.ASSIGNS)
-def test_ring_share_split_and_resume_unsplit(assign):
-    K.test_ring_share_split_and_resume("bf16", assign)
+@pytest.mark.parametrize("in_dt", ["bf16", "f32"])
+def test_ring_share_split_and_resume_unsplit(assign, in_dt):
+    K.test_ring_share_split_and_resume(in_dt, assign)
 
 
 @pytest.mark.usefixtures("never_split")
@@ -74,8 +77,9 @@ def test_ring_share_grouped_query_unsplit(assign, h, h_kv):
 @pytest.mark.parametrize("case", K.BLOCK_CASES, ids=[f"c{i}" for i in range(len(K.BLOCK_CASES))])
 @pytest.mark.parametrize("o_dt", ["bf16", "f32"])
 @pytest.mark.parametrize("d", [128, 64])
-def test_block_attn_parity_unsplit(case, o_dt, d):
-    K.test_block_attn_parity(case, "bf16", o_dt, d)
+@pytest.mark.parametrize("in_dt", ["bf16", "f32"])
+def test_block_attn_parity_unsplit(case, o_dt, d, in_dt):
+    K.test_block_attn_parity(case, in_dt, o_dt, d)
 
 
 @pytest.mark.usefixtures("never_split")
