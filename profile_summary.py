@@ -18,7 +18,8 @@
            (``*_counter_collection.csv``), workloads told apart by run order as in ``trace``.
            ``MfmaUtil`` (rocprofiler's derived counter: matrix-core busy cycles over active
            cycles of every SIMD) is shown in percent; ``SQ_INSTS_VALU_MFMA_MOPS_BF16`` times 512
-           is the bf16 matrix-core FLOP count each dispatch executed.
+           is the bf16 matrix-core FLOP count each dispatch executed; with TCC_HIT_sum and
+           TCC_MISS_sum the L2 hit rate is shown as well.
   hbm      HBM bandwidth of named kernels: mean duration from a kernel trace, algorithmic
            bytes per dispatch as given, and the bytes the counters saw (FETCH_SIZE and
            WRITE_SIZE runs, each scaled by what it reads for a plain device copy of known size
@@ -154,8 +155,10 @@ def pmc(args):
     names = sorted({c for r in disp_rows for c in r["_counters"]})
     lines = [f"# {args.title}", "", f"Command: `{args.cmd}`", "",
              "| kernel | grid (threads) | workload | dispatches | " + " | ".join(names) +
-             (" | bf16 MFMA TFLOP per dispatch" if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in names else "") + " |",
-             "|---|---|---|---|" + "---|" * len(names) + ("---|" if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in names else "")]
+             (" | bf16 MFMA TFLOP per dispatch" if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in names else "") +
+             (" | L2 hit %" if {"TCC_HIT_sum", "TCC_MISS_sum"} <= set(names) else "") + " |",
+             "|---|---|---|---|" + "---|" * len(names) + ("---|" if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in names else "") +
+             ("---|" if {"TCC_HIT_sum", "TCC_MISS_sum"} <= set(names) else "")]
     for (k, g, lab), v in sorted(groups.items(), key=lambda kv: (kv[0][0], -kv[0][1], kv[0][2])):
         if args.kernel and not any(k.startswith(x) for x in args.kernel):
             continue
@@ -167,6 +170,10 @@ def pmc(args):
         if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in names:
             mops = statistics.mean([r["_counters"]["SQ_INSTS_VALU_MFMA_MOPS_BF16"] for r in v])
             cells.append(f"{mops * 512 / 1e12:.4f}")
+        if {"TCC_HIT_sum", "TCC_MISS_sum"} <= set(names):
+            hit = sum(r["_counters"].get("TCC_HIT_sum", 0.0) for r in v)
+            miss = sum(r["_counters"].get("TCC_MISS_sum", 0.0) for r in v)
+            cells.append(f"{100 * hit / max(hit + miss, 1.0):.1f}")
         lines.append(f"| {k} | {g} | {lab} | {len(v)} | " + " | ".join(cells) + " |")
     text = "\n".join(lines) + "\n"
     if args.note:
