@@ -148,7 +148,12 @@ size_t ra_ring_share_workspace_bytes(int64_t B, int64_t H, int64_t S_loc, int64_
  *                        NULL when start_step == 0 and num_steps == N (the state then stays
  *                        in registers). A call that ends before step N stores the state in
  *                        ws; a call with start_step > 0 resumes from it. The state is
- *                        opaque, valid only for the same q, in_dtype, scale and shape.
+ *                        opaque (its layout depends on in_dtype) and valid only for the same
+ *                        q, in_dtype, scale, shape, assignment, mask, N and rank. The library
+ *                        records these (on the host, per workspace address) for every call
+ *                        that stores a state, and a resume returns RA_ERR_INVALID_ARG when
+ *                        ws holds no state stored in this process, when any of them differs,
+ *                        or when start_step is not the step the stored state ends at.
  * The result does not depend on how the N steps are split across calls, up to rounding.
  */
 int ra_ring_share(const void* q, const void* const* k_shares, const void* const* v_shares,

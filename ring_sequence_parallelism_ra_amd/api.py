@@ -38,6 +38,16 @@ def _need(t, name):
         raise ValueError(f"{name} must be a device tensor")
 
 
+def _expect(t, name, shape, dtype):
+    """Shape and dtype of a caller-supplied tensor, checked before anything is launched: the
+    library reads and writes exactly these extents in these element sizes."""
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    dts = dtype if isinstance(dtype, tuple) else (dtype,)
+    if t.dtype not in dts:
+        raise ValueError(f"{name} must be {' or '.join(str(d) for d in dts)}, got {t.dtype}")
+
+
 def _shard(sh):
     if sh is None:
         return None
@@ -50,13 +60,19 @@ def block_attn_fwd(q, k, v, *, causal=False, q_shard=None, kv_shard=None, scale=
                    o=None, lse=None, stream=None):
     """O, LSE of q [B,Sq,H,D] against one KV block k, v [B,Sk,H_kv,D] (H_kv dividing H: grouped-
     query attention); see ra_block_attn_fwd."""
-    for t, n in ((q, "q"), (k, "k"), (v, "v")):
-        _need(t, n)
     b, sq, h, d = q.shape
     sk, hkv = k.shape[1], k.shape[2]
-    if k.shape != (b, sk, hkv, d) or v.shape != k.shape or k.dtype != q.dtype or v.dtype != q.dtype:
-        raise ValueError("k/v must be [B, Sk, H_kv, D] with q's B, D and dtype")
-    od = out_dtype or q.dtype
+    _expect(q, "q", q.shape, tuple(_DT))
+    _expect(k, "k", (b, sk, hkv, d), q.dtype)
+    _expect(v, "v", k.shape, q.dtype)
+    od = out_dtype or (o.dtype if o is not None else q.dtype)
+    if o is not None:
+        _expect(o, "o", (b, sq, h, d), od)
+    if lse is not None:
+        _expect(lse, "lse", (b, h, sq), torch.float32)
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (lse, "lse")):
+        if t is not None:
+            _need(t, n)
     if o is None:
         o = torch.empty((b, sq, h, d), dtype=od, device=q.device)
     if lse is None:
@@ -80,25 +96,30 @@ def prepare_ring_share(q, k_shares, v_shares, rank, *, assign="contiguous", caus
                        stream=None):
     """Marshal the arguments of ra_ring_share once; returns (call, o, lse) where ``call()``
     enqueues the whole ring loop on the stream (for repeated launches)."""
-    _need(q, "q")
     b, s, h, d = q.shape
+    _expect(q, "q", q.shape, tuple(_DT))
     n = len(k_shares)
     if len(v_shares) != n:
         raise ValueError("k_shares and v_shares differ in length")
     hkv = k_shares[0].shape[2] if n else h
     for t in list(k_shares) + list(v_shares):
-        _need(t, "share")
-        if t.shape != (b, s, hkv, d) or t.dtype != q.dtype:
-            raise ValueError("every K/V share must be [B, S_loc, H_kv, D] with q's B, S_loc, D and dtype")
+        _expect(t, "every K/V share", (b, s, hkv, d), q.dtype)
     num = n - start_step if num_steps is None else num_steps
-    od = out_dtype or q.dtype
+    od = out_dtype or (o.dtype if o is not None else q.dtype)
+    if o is not None:
+        _expect(o, "o", (b, s, h, d), od)
+    if lse is not None:
+        _expect(lse, "lse", (b, h, s), torch.float32)
+    for t in [q, o, lse, ws] + list(k_shares) + list(v_shares):
+        if t is not None:
+            _need(t, "q/o/lse/ws/share")
     if o is None:
         o = torch.empty((b, s, h, d), dtype=od, device=q.device)
     if lse is None:
         lse = torch.empty((b, h, s), dtype=torch.float32, device=q.device)
     kp = (ctypes.c_void_p * n)(*[t.data_ptr() for t in k_shares])
     vp = (ctypes.c_void_p * n)(*[t.data_ptr() for t in v_shares])
-    ws_p, ws_n = (_p(ws), ws.numel()) if ws is not None else (None, 0)
+    ws_p, ws_n = (_p(ws), ws.numel() * ws.element_size()) if ws is not None else (None, 0)
     args = (_p(q), kp, vp, _p(o), _p(lse), b, h, hkv, s, d, n, rank, ASSIGN.get(assign, assign),
             1 if causal else 0, _dt(q), _dt(o), float(scale), start_step, num, ws_p, ws_n,
             _stream(stream))
@@ -123,19 +144,21 @@ def ring_share_bwd(q, k_shares, v_shares, o, lse, dout, rank, *, assign="contigu
     """Gradients of ``ring_share``'s output: returns (dq [B,S,H,D], dk list, dv list), fp32, where
     dk[i] / dv[i] [B,S,H_kv,D] are the gradients with respect to rank i's K/V share from this
     rank's queries; see ra_ring_share_bwd."""
-    for t, nm in ((q, "q"), (o, "o"), (lse, "lse"), (dout, "dout")):
-        _need(t, nm)
     b, s, h, d = q.shape
     n = len(k_shares)
     if len(v_shares) != n or n == 0:
         raise ValueError("k_shares and v_shares must be non-empty and of equal length")
     hkv = k_shares[0].shape[2]
+    # the library reads q, o, dout and the shares as bf16 and lse as fp32: a forward output
+    # kept in fp32 must be rounded to bf16 by the caller first
+    _expect(q, "q", (b, s, h, d), torch.bfloat16)
+    _expect(o, "o", (b, s, h, d), torch.bfloat16)
+    _expect(dout, "dout", (b, s, h, d), torch.bfloat16)
+    _expect(lse, "lse", (b, h, s), torch.float32)
     for t in list(k_shares) + list(v_shares):
-        _need(t, "share")
-        if t.shape != (b, s, hkv, d) or t.dtype != q.dtype:
-            raise ValueError("every K/V share must be [B, S_loc, H_kv, D] with q's B, S_loc, D and dtype")
-    if o.shape != q.shape or dout.shape != q.shape or lse.shape != (b, h, s):
-        raise ValueError("o and dout must match q; lse must be [B, H, S_loc]")
+        _expect(t, "every K/V share", (b, s, hkv, d), torch.bfloat16)
+    for t in [q, o, lse, dout] + list(k_shares) + list(v_shares):
+        _need(t, "q/o/lse/dout/share")
     dq = torch.empty((b, s, h, d), dtype=torch.float32, device=q.device)
     dk = [torch.empty((b, s, hkv, d), dtype=torch.float32, device=q.device) for _ in range(n)]
     dv = [torch.empty((b, s, hkv, d), dtype=torch.float32, device=q.device) for _ in range(n)]
@@ -169,26 +192,29 @@ def usp_local_step(q_stack, k_heads, v_heads, ulysses_rank, ring_rank, *, out=No
 
     Returns (out, O [B, L/r, H/u, D], LSE [B, H/u, L/r]).
     """
-    _need(q_stack, "q_stack")
     u, b, s, h, d = q_stack.shape
+    od = out_dtype or q_stack.dtype
+    if out is not None:
+        _expect(out, "out", (u, b, s, h, d), od)
+    _need(q_stack, "q_stack")
     qh = seq2head_permute(q_stack, ulysses_rank, stream=stream)
     o, lse = ring_share(qh, k_heads, v_heads, ring_rank, assign="zigzag", causal=True, scale=scale,
                         out_dtype=out_dtype, stream=stream)
     if out is None:
-        out = torch.zeros((u, b, s, h, d), dtype=o.dtype, device=q_stack.device)
+        out = torch.zeros((u, b, s, h, d), dtype=od, device=q_stack.device)
     head2seq_permute(o, ulysses_rank, out, stream=stream)
     return out, o, lse
 
 
 def lse_merge(o_acc, lse_acc, o_blk, lse_blk, stream=None):
     """In-place merge of (o_blk, lse_blk) into (o_acc, lse_acc); see ra_lse_merge."""
+    b, s, h, d = o_acc.shape
+    _expect(o_acc, "o_acc", o_acc.shape, tuple(_DT))
+    _expect(o_blk, "o_blk", o_acc.shape, tuple(_DT))
+    _expect(lse_acc, "lse_acc", (b, h, s), torch.float32)
+    _expect(lse_blk, "lse_blk", (b, h, s), torch.float32)
     for t, nme in ((o_acc, "o_acc"), (lse_acc, "lse_acc"), (o_blk, "o_blk"), (lse_blk, "lse_blk")):
         _need(t, nme)
-    b, s, h, d = o_acc.shape
-    if o_blk.shape != o_acc.shape or lse_acc.shape != (b, h, s) or lse_blk.shape != (b, h, s):
-        raise ValueError("shape mismatch")
-    if lse_acc.dtype != torch.float32 or lse_blk.dtype != torch.float32:
-        raise ValueError("lse tensors must be float32")
     check(lib.ra_lse_merge(_p(o_acc), _p(lse_acc), _p(o_blk), _p(lse_blk), b, h, s, d, _dt(o_acc),
                            _dt(o_blk), _stream(stream)))
     return o_acc, lse_acc
@@ -197,9 +223,15 @@ def lse_merge(o_acc, lse_acc, o_blk, lse_blk, stream=None):
 def seq2head_permute(x, dst_rank, out=None, stream=None):
     """x [P, B, S_loc, H, D] -> [B, P*S_loc, H/P, D] for dst_rank (or the stack of all ranks
     [P, B, P*S_loc, H/P, D] for dst_rank=-1); see ra_seq2head_permute."""
-    _need(x, "x")
     p, b, s, h, d = x.shape
+    _expect(x, "x", x.shape, tuple(_DT))
+    if h % p:
+        raise ValueError(f"P={p} does not divide H={h}")
     shape = (b, p * s, h // p, d) if dst_rank >= 0 else (p, b, p * s, h // p, d)
+    if out is not None:
+        _expect(out, "out", shape, x.dtype)
+        _need(out, "out")
+    _need(x, "x")
     if out is None:
         out = torch.empty(shape, dtype=x.dtype, device=x.device)
     check(lib.ra_seq2head_permute(_p(x), _p(out), b, p, s, h, d, _dt(x), dst_rank, 0, _stream(stream)))
@@ -209,9 +241,13 @@ def seq2head_permute(x, dst_rank, out=None, stream=None):
 def head2seq_permute(y, dst_rank, out, stream=None):
     """Inverse: write y (dst_rank's head-sharded tensor, or the stack) back into
     out [P, B, S_loc, H, D], touching only dst_rank's heads (all for -1)."""
+    p, b, s, h, d = out.shape
+    _expect(out, "out", out.shape, tuple(_DT))
+    if h % p:
+        raise ValueError(f"P={p} does not divide H={h}")
+    _expect(y, "y", (b, p * s, h // p, d) if dst_rank >= 0 else (p, b, p * s, h // p, d), out.dtype)
     _need(y, "y")
     _need(out, "out")
-    p, b, s, h, d = out.shape
     check(lib.ra_seq2head_permute(_p(y), _p(out), b, p, s, h, d, _dt(out), dst_rank, 1, _stream(stream)))
     return out
 

@@ -8,6 +8,9 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+#include <unordered_map>
+
 #include "ra_internal.h"
 
 namespace {
@@ -77,6 +80,49 @@ int check_kv_heads(int64_t H, int64_t H_kv) {
   if (H % H_kv)
     return fail(RA_ERR_SHAPE, "H_kv=%lld does not divide H=%lld", (long long)H_kv, (long long)H);
   return RA_OK;
+}
+
+// What a resume workspace holds. The running state's layout depends on the kernel that wrote
+// it (the bf16 kernel keeps the running max in log2 units of scaled logits, the fp32 kernel in
+// natural units), so a state may only be resumed by a call with the same arguments, at the step
+// where the storing call stopped. The record is kept on the host, per workspace address, for
+// every call that stores a state; a resume is checked against it before anything is launched.
+struct WsTag {
+  int in_dtype, assign, causal, N, rank;
+  int64_t B, H, H_kv, S, D;
+  uint32_t scale_bits;
+  int next_step;  // the first step the stored state has not folded in
+};
+
+std::mutex g_ws_mu;
+std::unordered_map<uintptr_t, WsTag>& ws_tags() {
+  static std::unordered_map<uintptr_t, WsTag> m;
+  return m;
+}
+
+// RA_OK if `want` (with next_step = the resuming call's start_step) may resume the state in ws.
+int check_resume(const void* ws, const WsTag& want) {
+  std::lock_guard<std::mutex> lk(g_ws_mu);
+  auto it = ws_tags().find((uintptr_t)ws);
+  if (it == ws_tags().end())
+    return fail(RA_ERR_INVALID_ARG, "resume: no running state was stored in this workspace by this process");
+  const WsTag& t = it->second;
+  if (t.in_dtype != want.in_dtype)
+    return fail(RA_ERR_INVALID_ARG, "resume: state stored with in_dtype %d, resumed with %d", t.in_dtype, want.in_dtype);
+  if (t.scale_bits != want.scale_bits) return fail(RA_ERR_INVALID_ARG, "resume: state stored with another scale");
+  if (t.assign != want.assign || t.causal != want.causal || t.N != want.N || t.rank != want.rank)
+    return fail(RA_ERR_INVALID_ARG, "resume: state stored for another ring (assignment, mask, N or rank)");
+  if (t.B != want.B || t.H != want.H || t.H_kv != want.H_kv || t.S != want.S || t.D != want.D)
+    return fail(RA_ERR_INVALID_ARG, "resume: state stored for another shape");
+  if (t.next_step != want.next_step)
+    return fail(RA_ERR_INVALID_ARG, "resume: state covers steps up to %d, call starts at step %d", t.next_step,
+                want.next_step);
+  return RA_OK;
+}
+
+void record_state(const void* ws, const WsTag& tag) {
+  std::lock_guard<std::mutex> lk(g_ws_mu);
+  ws_tags()[(uintptr_t)ws] = tag;
 }
 
 int launch_attn(const ra::AttnArgs& a, int D, int in_dtype, int o_dtype, hipStream_t stream) {
@@ -201,6 +247,25 @@ int ra_ring_share(const void* q, const void* const* k_shares, const void* const*
   }
   if (empty) return ok();
 
+  const float scale_eff = scale > 0.f ? scale : (float)(1.0 / sqrt((double)D));
+  WsTag tag;
+  memset(&tag, 0, sizeof tag);
+  tag.in_dtype = in_dtype;
+  tag.assign = assign;
+  tag.causal = causal ? 1 : 0;
+  tag.N = N;
+  tag.rank = rank;
+  tag.B = B;
+  tag.H = H;
+  tag.H_kv = H_kv;
+  tag.S = S_loc;
+  tag.D = D;
+  memcpy(&tag.scale_bits, &scale_eff, sizeof scale_eff);
+  if (load_state) {
+    tag.next_step = start_step;
+    if ((rc = check_resume(ws, tag))) return rc;
+  }
+
   ra::AttnArgs a;
   memset(&a, 0, sizeof a);
   a.q = q;
@@ -231,12 +296,17 @@ int ra_ring_share(const void* q, const void* const* k_shares, const void* const*
   a.causal = causal ? 1 : 0;
   a.load_state = load_state ? 1 : 0;
   a.store_final = store_final ? 1 : 0;
-  a.scale = scale > 0.f ? scale : (float)(1.0 / sqrt((double)D));
+  a.scale = scale_eff;
   a.qpos = ra::make_pos(assign, N, rank, L);
   a.kv_assign = assign;
   a.kv_world = N;
   a.kv_len = L;
-  return launch_attn(a, (int)D, in_dtype, o_dtype, stream);
+  if ((rc = launch_attn(a, (int)D, in_dtype, o_dtype, stream))) return rc;
+  if (!store_final) {
+    tag.next_step = start_step + num_steps;
+    record_state(ws, tag);
+  }
+  return ok();
 }
 
 size_t ra_ring_share_bwd_workspace_bytes(int64_t B, int64_t H, int64_t S_loc) {

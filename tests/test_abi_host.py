@@ -117,6 +117,9 @@ def test_ring_share_validation():
     need = lib.ra_ring_share_workspace_bytes(1, 2, 64, 128)
     assert need == 4 * 64 * 2 * 128 + 16 * 2 * 64
     assert call_ring(start=1, num=3, ws=FAKE, wsb=need - 4) == INVALID
+    # a resume needs a state this process stored in that workspace
+    assert call_ring(start=1, num=3, ws=ctypes.c_void_p(0x20000), wsb=need) == INVALID
+    assert "no running state" in _lib.last_error()
     assert call_ring(D=64, ind=5) == UNSUP
     assert call_ring(H=4, Hkv=3) == SHAPE
     assert call_ring(H=4, Hkv=0) == INVALID

@@ -1,4 +1,5 @@
-"""Pins for oracle.permute: index formula on arange payloads, head ownership, exact inverses."""
+"""Pins for oracle.permute: the whole-tensor statement of [Digest] §5.1 (shares of a global
+tensor in, head slices of the same global tensor out), head ownership, exact inverses."""
 import numpy as np
 import pytest
 
@@ -16,16 +17,29 @@ def test_head_ownership_page(golden):
         assert y.shape == (1, p * s, h // p, d)
 
 
-def test_sequence_order_by_source_rank():
-    p, b, s, h, d = 4, 2, 3, 8, 5
-    x = np.arange(p * b * s * h * d).reshape(p, b, s, h, d)
+@pytest.mark.parametrize("p,hmul,s", [(2, 1, 3), (4, 2, 5), (8, 1, 2)])
+def test_global_tensor_identity(p, hmul, s):
+    # [Digest] §5.1 stated on a whole tensor: the sequence [B, L, H, D] is cut into P contiguous
+    # runs of L/P rows (rank src holds rows src*L/P ..), every head; after the all-to-all, rank p
+    # holds the WHOLE sequence in its natural order for heads [p*H/P, (p+1)*H/P). So the
+    # layout change of the stacked shares must equal plain slicing of the global tensor.
+    b, h, d = 2, p * hmul, 3
+    L = p * s
+    g = np.random.default_rng(p * 100 + s).integers(-1000, 1000, size=(b, L, h, d))
+    stack = np.stack([g[:, src * s:(src + 1) * s] for src in range(p)])   # [P, B, L/P, H, D]
+    hp = h // p
     for dst in range(p):
-        y = U.seq2head(x, dst)
-        hp = h // p
-        for src in range(p):
-            for si in range(s):
-                for hh in range(hp):
-                    assert np.array_equal(y[:, src * s + si, hh], x[src, :, si, dst * hp + hh])
+        assert np.array_equal(U.seq2head(stack, dst), g[:, :, dst * hp:(dst + 1) * hp])
+    assert np.array_equal(U.seq2head(stack, -1), np.stack([g[:, :, q * hp:(q + 1) * hp] for q in range(p)]))
+    # and the reverse: writing rank dst's head slice of the global tensor back yields the shares
+    # with exactly that head slice filled in, in sequence order
+    for dst in range(p):
+        back = U.head2seq(g[:, :, dst * hp:(dst + 1) * hp], dst, np.zeros_like(stack))
+        want = np.zeros_like(stack)
+        want[:, :, :, dst * hp:(dst + 1) * hp] = stack[:, :, :, dst * hp:(dst + 1) * hp]
+        assert np.array_equal(back, want)
+    every = U.head2seq(np.stack([g[:, :, q * hp:(q + 1) * hp] for q in range(p)]), -1, np.zeros_like(stack))
+    assert np.array_equal(every, stack)
 
 
 @pytest.mark.parametrize("p", [2, 4, 8])
