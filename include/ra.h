@@ -238,6 +238,33 @@ int ra_debug_positions(const ra_shard* sh, int64_t* out, hipStream_t stream);
 int ra_debug_mask(const ra_shard* q_sh, const ra_shard* kv_sh, int64_t Sq, int64_t Sk,
                   uint8_t* out, hipStream_t stream);
 
+/*
+ * Device-side tile counts (debug hook, not part of the hot path). Tile skipping is what makes
+ * causal work about half of the full product (the lower-triangular causal matrix of [Digest]
+ * §3.4): these calls show which K/V tiles the bf16 kernel actually visits.
+ *
+ * ra_debug_tile_count_slots: int32 slots ra_debug_tile_counts writes for a share of S_loc query
+ * rows: ceil(S_loc / block_m) * B * H * 16 (block_m from ra_tile_shape, 128 for bf16).
+ *
+ * ra_debug_tile_counts: the same computation and outputs as ra_ring_share over every ring step
+ * (start_step 0, num_steps N, no workspace) with bf16 inputs, run through a copy of the bf16
+ * kernel that also counts, for every wave, the K/V tiles (block_n = 64 keys) it folds into its
+ * 32 query rows and, among those, the tiles on which it evaluates the mask (a tile is masked by
+ * a wave when it is the ragged last tile of a share or when the wave's first query row does not
+ * see the tile's last key). The workgroup layout (one query tile, key split, paired tiles) is
+ * chosen exactly as for ra_ring_share. Output counts, int32 [ceil(S_loc/128), B, H, 8, 2]:
+ * [qt, b, h, w, 0] = tiles folded in by wave slot w of query tile qt, [.., 1] = tiles it masked.
+ * Wave slots 0-3 are the four waves of the first (or only) wave group, 4-7 those of the second
+ * group of a key-split workgroup (zero otherwise); a wave whose rows all lie past S_loc counts
+ * nothing. counts is a device buffer of counts_len >= ra_debug_tile_count_slots(..) slots,
+ * 16-byte aligned; every slot is written. Other arguments and errors as in ra_ring_share.
+ */
+int64_t ra_debug_tile_count_slots(int64_t B, int64_t H, int64_t S_loc);
+int ra_debug_tile_counts(const void* q, const void* const* k_shares, const void* const* v_shares,
+                         void* o, float* lse, int64_t B, int64_t H, int64_t H_kv, int64_t S_loc,
+                         int64_t D, int N, int rank, int assign, int causal, int o_dtype, float scale,
+                         int32_t* counts, int64_t counts_len, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -76,3 +76,57 @@ def delta_rows(o, do):
     o = np.asarray(o, dtype=np.float64)
     do = np.asarray(do, dtype=np.float64)
     return np.einsum("bshd,bshd->bhs", o, do)
+
+
+def attention_bwd_magnitudes(q, k, v, do, qpos=None, kpos=None, causal: bool = False, scale=None,
+                             delta_err=None, row_chunk: int = 256):
+    """Entry-wise magnitudes of the sums that make up each gradient of ``attention_bwd``, for
+    error bounds: the same chain rule with every term replaced by its absolute value.
+
+        A_dq[i] = scale * sum_j |dS_ij| |k_j|       A_dk[j] = scale * sum_i |dS_ij| |q_i|
+        E_dq[i] = scale * e_i sum_j P_ij |k_j|       E_dk[j] = scale * sum_i e_i P_ij |q_i|
+        A_dv[j] = sum_i P_ij |dO_i|
+
+    (|.| taken element by element along the head dimension). ``delta_err`` [B, H, Sq] is a
+    per-row bound e_i on an error in Delta_i (zero when omitted): a change of Delta_i by e
+    changes dS_ij by P_ij e. A bounded relative error u on every term of a sum moves it by at
+    most u times these magnitudes. Returns (A_dq, E_dq, A_dk, E_dk, A_dv) in the gradients'
+    shapes, float64."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    do = np.asarray(do, dtype=np.float64)
+    b_, sq, h_, d = q.shape
+    sk, h_kv = k.shape[1], k.shape[2]
+    group = h_ // h_kv
+    if scale is None or scale <= 0:
+        scale = 1.0 / math.sqrt(d)
+    if causal:
+        qpos = np.asarray(qpos, dtype=np.int64)
+        kpos = np.asarray(kpos, dtype=np.int64)
+    e_all = np.zeros((b_, h_, sq)) if delta_err is None else np.asarray(delta_err, dtype=np.float64)
+    a_dq, e_dq = np.zeros_like(q), np.zeros_like(q)
+    a_dk, e_dk, a_dv = np.zeros_like(k), np.zeros_like(k), np.zeros_like(v)
+    for b in range(b_):
+        for h in range(h_):
+            hk = h // group
+            kk, vv = k[b, :, hk], v[b, :, hk]
+            for r0 in range(0, sq, row_chunk):
+                r1 = min(sq, r0 + row_chunk)
+                mask = visible(qpos[r0:r1], kpos, True) if causal else np.ones((r1 - r0, sk), dtype=bool)
+                s = np.where(mask, (q[b, r0:r1, h] @ kk.T) * scale, -np.inf)
+                m = s.max(axis=1) if sk else np.full(r1 - r0, -np.inf)
+                has = np.isfinite(m)
+                p = np.exp(s - np.where(has, m, 0.0)[:, None])
+                p /= np.where(has, p.sum(axis=1), 1.0)[:, None]
+                g = do[b, r0:r1, h]
+                dp = g @ vv.T
+                ds = p * (dp - (p * dp).sum(axis=1)[:, None])
+                e = e_all[b, h, r0:r1]
+                aq = np.abs(q[b, r0:r1, h])
+                a_dq[b, r0:r1, h] = scale * (np.abs(ds) @ np.abs(kk))
+                e_dq[b, r0:r1, h] = scale * e[:, None] * (p @ np.abs(kk))
+                a_dk[b, :, hk] += scale * (np.abs(ds).T @ aq)
+                e_dk[b, :, hk] += scale * ((p * e[:, None]).T @ aq)
+                a_dv[b, :, hk] += p.T @ np.abs(g)
+    return a_dq, e_dq, a_dk, e_dk, a_dv

@@ -29,7 +29,8 @@ STATUS = {0: "RA_OK", -1: "RA_ERR_INVALID_ARG", -2: "RA_ERR_UNSUPPORTED", -3: "R
 # Every function the header declares, in declaration order.
 EXPORTS = ["ra_block_attn_fwd", "ra_lse_merge", "ra_ring_share_workspace_bytes", "ra_ring_share",
            "ra_ring_share_bwd_workspace_bytes", "ra_ring_share_bwd", "ra_seq2head_permute", "ra_last_error",
-           "ra_share_work", "ra_tile_shape", "ra_debug_positions", "ra_debug_mask"]
+           "ra_share_work", "ra_tile_shape", "ra_debug_positions", "ra_debug_mask", "ra_debug_tile_count_slots",
+           "ra_debug_tile_counts"]
 
 
 class RaError(RuntimeError):
@@ -66,6 +67,8 @@ def _load():
         "ra_tile_shape": (I, [I, I64, ctypes.POINTER(I64), ctypes.POINTER(I64)]),
         "ra_debug_positions": (I, [SH, P, P]),
         "ra_debug_mask": (I, [SH, SH, I64, I64, P, P]),
+        "ra_debug_tile_count_slots": (I64, [I64, I64, I64]),
+        "ra_debug_tile_counts": (I, [P, P, P, P, P, I64, I64, I64, I64, I64, I, I, I, I, I, F, P, I64, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)

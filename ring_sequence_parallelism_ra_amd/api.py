@@ -279,5 +279,33 @@ def debug_mask(q_shard, kv_shard, Sq, Sk, device="cuda", stream=None):
     return out
 
 
+def debug_tile_counts(q, k_shares, v_shares, rank, *, assign="contiguous", causal=True, scale=0.0,
+                      out_dtype=None, stream=None):
+    """ring_share through the tile-counting copy of the bf16 kernel; returns (O, LSE, counts) with
+    counts int32 [ceil(S_loc/128), B, H, 8, 2] (per wave slot: tiles folded in, tiles masked);
+    see ra_debug_tile_counts."""
+    b, s, h, d = q.shape
+    _expect(q, "q", q.shape, torch.bfloat16)
+    n = len(k_shares)
+    if len(v_shares) != n or n == 0:
+        raise ValueError("k_shares and v_shares must be non-empty and of equal length")
+    hkv = k_shares[0].shape[2]
+    for t in list(k_shares) + list(v_shares):
+        _expect(t, "every K/V share", (b, s, hkv, d), torch.bfloat16)
+    for t in [q] + list(k_shares) + list(v_shares):
+        _need(t, "q/share")
+    od = out_dtype or q.dtype
+    o = torch.empty((b, s, h, d), dtype=od, device=q.device)
+    lse = torch.empty((b, h, s), dtype=torch.float32, device=q.device)
+    slots = int(lib.ra_debug_tile_count_slots(b, h, s))
+    counts = torch.empty(max(slots, 4), dtype=torch.int32, device=q.device)
+    kp = (ctypes.c_void_p * n)(*[t.data_ptr() for t in k_shares])
+    vp = (ctypes.c_void_p * n)(*[t.data_ptr() for t in v_shares])
+    check(lib.ra_debug_tile_counts(_p(q), kp, vp, _p(o), _p(lse), b, h, hkv, s, d, n, rank, ASSIGN.get(assign, assign),
+                                   1 if causal else 0, _dt(o), float(scale), _p(counts), counts.numel(),
+                                   _stream(stream)))
+    return o, lse, counts[:slots].view(-1, b, h, 8, 2)
+
+
 def torch_dtype(code: int):
     return _TORCH_DT[code]

@@ -178,7 +178,9 @@ __device__ __forceinline__ void sched_chunk(std::integer_sequence<int, I...>) {
 // so the workgroups resident at once read the same key tiles at the same time and finish
 // together (unpaired, the striped share's late-starting workgroups walk out of step with the
 // running ones and miss in L2).
-template <int D, class Out, int KVS, int PAIR>
+// DBG = 1 (debug hook only, never a product launch): every wave also counts the K/V tiles it
+// folds in and those on which it evaluates the mask, and writes both to a.dbg_counts.
+template <int D, class Out, int KVS, int PAIR, int DBG>
 __global__ __launch_bounds__(NT * KVS, QB == 1 ? RA_ATTN_WAVES_PER_SIMD : 1) void attn_bf16_kernel(const AttnArgs a) {
   using C = Cfg<D>;
   static_assert(KVS == 1 || (KVS == 2 && QB == 1), "the key split merges one 32-row block per wave");
@@ -265,16 +267,23 @@ static int pair_override() {
   return 0;
 }
 
-template <int KVS, int PAIR>
-static void launch(const AttnArgs& a, int D, int o_dtype, dim3 g, hipStream_t stream) {
+template <int KVS, int PAIR, int DBG>
+static void launch_dbg(const AttnArgs& a, int D, int o_dtype, dim3 g, hipStream_t stream) {
   dim3 blk(NT * KVS);
   if (D == 128) {
-    if (o_dtype == RA_BF16) hipLaunchKernelGGL((attn_bf16_kernel<128, OutBf16, KVS, PAIR>), g, blk, 0, stream, a);
-    else hipLaunchKernelGGL((attn_bf16_kernel<128, OutF32, KVS, PAIR>), g, blk, 0, stream, a);
+    if (o_dtype == RA_BF16) hipLaunchKernelGGL((attn_bf16_kernel<128, OutBf16, KVS, PAIR, DBG>), g, blk, 0, stream, a);
+    else hipLaunchKernelGGL((attn_bf16_kernel<128, OutF32, KVS, PAIR, DBG>), g, blk, 0, stream, a);
   } else {
-    if (o_dtype == RA_BF16) hipLaunchKernelGGL((attn_bf16_kernel<64, OutBf16, KVS, PAIR>), g, blk, 0, stream, a);
-    else hipLaunchKernelGGL((attn_bf16_kernel<64, OutF32, KVS, PAIR>), g, blk, 0, stream, a);
+    if (o_dtype == RA_BF16) hipLaunchKernelGGL((attn_bf16_kernel<64, OutBf16, KVS, PAIR, DBG>), g, blk, 0, stream, a);
+    else hipLaunchKernelGGL((attn_bf16_kernel<64, OutF32, KVS, PAIR, DBG>), g, blk, 0, stream, a);
   }
+}
+
+// The counting copy is chosen only when a debug buffer is passed; the layout choice is the same.
+template <int KVS, int PAIR>
+static void launch(const AttnArgs& a, int D, int o_dtype, dim3 g, hipStream_t stream) {
+  if (a.dbg_counts) launch_dbg<KVS, PAIR, 1>(a, D, o_dtype, g, stream);
+  else launch_dbg<KVS, PAIR, 0>(a, D, o_dtype, g, stream);
 }
 
 hipError_t launch_attn_bf16(const AttnArgs& a, int D, int o_dtype, hipStream_t stream) {

@@ -200,10 +200,16 @@ size_t ra_ring_share_workspace_bytes(int64_t B, int64_t H, int64_t S_loc, int64_
   return (size_t)4 * (size_t)(B * S_loc * H * D) + (size_t)16 * (size_t)(B * H * S_loc);
 }
 
-int ra_ring_share(const void* q, const void* const* k_shares, const void* const* v_shares, void* o,
-                  float* lse, int64_t B, int64_t H, int64_t H_kv, int64_t S_loc, int64_t D, int N,
-                  int rank, int assign, int causal, int in_dtype, int o_dtype, float scale,
-                  int start_step, int num_steps, void* ws, size_t ws_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// ra_ring_share, with the debug tile counter of the instrumented kernel when dbg is not null.
+int ring_share_impl(const void* q, const void* const* k_shares, const void* const* v_shares, void* o,
+                    float* lse, int64_t B, int64_t H, int64_t H_kv, int64_t S_loc, int64_t D, int N,
+                    int rank, int assign, int causal, int in_dtype, int o_dtype, float scale,
+                    int start_step, int num_steps, void* ws, size_t ws_bytes, int32_t* dbg,
+                    hipStream_t stream) {
   int rc = check_dims(B, H, S_loc, S_loc, D);
   if (rc) return rc;
   if ((rc = check_kv_heads(H, H_kv))) return rc;
@@ -301,12 +307,46 @@ int ra_ring_share(const void* q, const void* const* k_shares, const void* const*
   a.kv_assign = assign;
   a.kv_world = N;
   a.kv_len = L;
+  a.dbg_counts = dbg;
   if ((rc = launch_attn(a, (int)D, in_dtype, o_dtype, stream))) return rc;
   if (!store_final) {
     tag.next_step = start_step + num_steps;
     record_state(ws, tag);
   }
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int ra_ring_share(const void* q, const void* const* k_shares, const void* const* v_shares, void* o,
+                  float* lse, int64_t B, int64_t H, int64_t H_kv, int64_t S_loc, int64_t D, int N,
+                  int rank, int assign, int causal, int in_dtype, int o_dtype, float scale,
+                  int start_step, int num_steps, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return ring_share_impl(q, k_shares, v_shares, o, lse, B, H, H_kv, S_loc, D, N, rank, assign, causal,
+                         in_dtype, o_dtype, scale, start_step, num_steps, ws, ws_bytes, nullptr, stream);
+}
+
+int64_t ra_debug_tile_count_slots(int64_t B, int64_t H, int64_t S_loc) {
+  if (B < 0 || H < 0 || S_loc < 0) return 0;
+  return (S_loc + ra::kBf16BlockM - 1) / ra::kBf16BlockM * B * H * 16;
+}
+
+int ra_debug_tile_counts(const void* q, const void* const* k_shares, const void* const* v_shares, void* o,
+                         float* lse, int64_t B, int64_t H, int64_t H_kv, int64_t S_loc, int64_t D, int N,
+                         int rank, int assign, int causal, int o_dtype, float scale, int32_t* counts,
+                         int64_t counts_len, hipStream_t stream) {
+  if (B < 0 || H < 0 || S_loc < 0) return fail(RA_ERR_INVALID_ARG, "negative size");
+  const int64_t need = ra_debug_tile_count_slots(B, H, S_loc);
+  if (need > 0) {
+    if (!counts) return fail(RA_ERR_INVALID_ARG, "NULL counts buffer");
+    if (misaligned(counts)) return fail(RA_ERR_MISALIGNED, "counts not 16-byte aligned");
+    if (counts_len < need)
+      return fail(RA_ERR_INVALID_ARG, "counts holds %lld slots, %lld needed", (long long)counts_len, (long long)need);
+  }
+  return ring_share_impl(q, k_shares, v_shares, o, lse, B, H, H_kv, S_loc, D, N, rank, assign, causal, RA_BF16,
+                         o_dtype, scale, 0, N, nullptr, 0, counts, stream);
 }
 
 size_t ra_ring_share_bwd_workspace_bytes(int64_t B, int64_t H, int64_t S_loc) {

@@ -90,6 +90,10 @@ struct AttnArgs {
   int32_t kv_assign, kv_world;
   int64_t kv_len;       // global length of the KV rule (rank comes from kv_rank[s])
   float scale;          // logit scale (natural units)
+  // Debug only (null in every product call): per-wave tile counts of the instrumented kernel,
+  // int32 [ceil(Sq/BM), B, H, 8, 2]: for wave slot w (group * waves + wave) the K/V tiles it
+  // folded in and on how many of them it evaluated the mask.
+  int32_t* dbg_counts;
 };
 
 // Arguments of the backward launches (bf16 inputs, fp32 gradients; same layouts as AttnArgs).

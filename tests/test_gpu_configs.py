@@ -1,13 +1,16 @@
 """GPU parity on the workloads at their full sizes, in the launch configuration the
 benchmark times (one ra_ring_share call per rank share; the Ulysses permutes and one
 full-sequence causal ra_block_attn_fwd; the USP device step). The oracle checks every row of
-the small workloads and 512 seeded query rows (all heads) of the large ones."""
+the small workloads (the 4096-query striped shares included) and 512 seeded query rows (all
+heads) of the large ones; the headline share and the Ulysses attention also run with fp32
+output, held to the flat kernel bound."""
 import numpy as np
 import pytest
 import torch
 
 import synth
-from gpu_helpers import check, dev, host, say, shares, oracle_rows, values
+from gpu_helpers import (check, check_grad_entries, delta_error, dev, host, oracle_rows, oracle_share, per_head,
+                         say, shares, values)
 from oracle import attention as OA
 from oracle import backward as OB
 from oracle import permute as OU
@@ -72,34 +75,62 @@ def test_contig_rank7_full(o_dt):
     say(f"  max err O {eo:.3e} LSE {el:.3e}")
 
 
-def _sampled_ring(name, o_dt="bf16"):
+def _ring_inputs(name):
     w = synth.get(name)
     gq, gk, gv = synth.global_qkv(w)
     n, r, L = w.world, w.rank, w.global_len
-    say(f"{name}: inputs ready")
     pos = [OP.positions(w.assign, n, s, L) for s in range(n)]
     kd = [dev(np.ascontiguousarray(gk[:, p]), "bf16") for p in pos]
     vd = [dev(np.ascontiguousarray(gv[:, p]), "bf16") for p in pos]
     q_share = np.ascontiguousarray(gq[:, pos[r]])
-    o, lse = ra.ring_share(dev(q_share, "bf16"), kd, vd, r, assign=w.assign, causal=True,
+    return w, (gq, gk, gv), pos, q_share, kd, vd
+
+
+def _run_ring(w, q_share, kd, vd, o_dt):
+    o, lse = ra.ring_share(dev(q_share, "bf16"), kd, vd, w.rank, assign=w.assign, causal=True,
                            out_dtype=torch.bfloat16 if o_dt == "bf16" else torch.float32)
     torch.cuda.synchronize()
-    say(f"{name}: kernel done")
+    return o, lse
+
+
+def _sampled_ring(name, o_dts=("bf16",)):
+    """512 seeded rows (all heads) of a share too large for the full oracle, against one oracle
+    evaluation, for every output dtype in ``o_dts`` (fp32 output isolates the kernel's error
+    from the rounding of a bf16 result, and is held to the flat bound)."""
+    w, (gq, gk, gv), pos, q_share, kd, vd = _ring_inputs(name)
+    n, r, L = w.world, w.rank, w.global_len
+    say(f"{name}: inputs ready")
     chunk = L // (2 * n) if w.assign == "zigzag" else None
     rows = synth.sample_rows(1000 * w.number, w.share_len, chunk_len=chunk)
     o_ref, lse_ref = oracle_rows(values(q_share, "bf16"), values(gk, "bf16"), values(gv, "bf16"), pos[r][rows], rows)
-    eo, el = check(host(o)[:, rows], host(lse)[:, :, rows], o_ref, lse_ref, "bf16", o_dt, name)
-    say(f"  {len(rows)} rows x {w.heads} heads: max err O {eo:.3e} LSE {el:.3e}")
+    for o_dt in o_dts:
+        o, lse = _run_ring(w, q_share, kd, vd, o_dt)
+        say(f"{name} out={o_dt}: kernel done")
+        eo, el = check(host(o)[:, rows], host(lse)[:, :, rows], o_ref, lse_ref, "bf16", o_dt, f"{name} out={o_dt}")
+        say(f"  {len(rows)} rows x {w.heads} heads: max err O {eo:.3e} LSE {el:.3e}")
+
+
+_FULL_REF = {}
 
 
 @pytest.mark.parametrize("name", ["striped_rank0", "striped_rank0_std4"])
 @pytest.mark.parametrize("o_dt", ["bf16", "f32"])
-def test_striped_rank0_sampled(name, o_dt):
-    _sampled_ring(name, o_dt)
+def test_striped_rank0_full(name, o_dt):
+    # every row and head of rank 0's 4096-query share against the fp64 oracle, computed once per
+    # input variant and reused for both output dtypes
+    w, (gq, gk, gv), pos, q_share, kd, vd = _ring_inputs(name)
+    say(f"{name} out={o_dt}: inputs ready")
+    if name not in _FULL_REF:
+        _FULL_REF[name] = oracle_share(values(q_share, "bf16"), values(gk, "bf16"), values(gv, "bf16"), pos[w.rank])
+        say(f"{name}: oracle of all {w.share_len} rows x {w.heads} heads done")
+    o_ref, lse_ref = _FULL_REF[name]
+    o, lse = _run_ring(w, q_share, kd, vd, o_dt)
+    eo, el = check(o, lse, o_ref, lse_ref, "bf16", o_dt, f"{name} out={o_dt}")
+    say(f"  all rows: max err O {eo:.3e} LSE {el:.3e}")
 
 
 def test_zigzag_rank3_sampled():
-    _sampled_ring("zigzag_rank3")
+    _sampled_ring("zigzag_rank3", ("bf16", "f32"))
 
 
 def test_gqa_zigzag_rank3_sampled():
@@ -130,12 +161,19 @@ def test_ulysses_local():
         assert np.array_equal(got.cpu().view(torch.int16).numpy(), exp.view(np.int16))
     say("ulysses_local: permute bit-exact")
     full = ra.Shard("contiguous", 1, 0, L)
-    o, lse = ra.block_attn_fwd(perm[0], perm[1], perm[2], causal=True, q_shard=full, kv_shard=full)
-    torch.cuda.synchronize()
     rows = synth.sample_rows(1000 * w.number, L, tile=128)
     o_ref, lse_ref = oracle_rows(values(want[0], "bf16"), values(want[1], "bf16"), values(want[2], "bf16"), rows, rows)
+    # fp32 output first (the flat kernel bound), then the bf16 output the local step uses
+    o32, lse32 = ra.block_attn_fwd(perm[0], perm[1], perm[2], causal=True, q_shard=full, kv_shard=full,
+                                   out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    eo, el = check(host(o32)[:, rows], host(lse32)[:, :, rows], o_ref, lse_ref, "bf16", "f32", "ulysses attention f32")
+    say(f"  attention out=f32 {len(rows)} rows: max err O {eo:.3e} LSE {el:.3e}")
+    del o32, lse32
+    o, lse = ra.block_attn_fwd(perm[0], perm[1], perm[2], causal=True, q_shard=full, kv_shard=full)
+    torch.cuda.synchronize()
     eo, el = check(host(o)[:, rows], host(lse)[:, :, rows], o_ref, lse_ref, "bf16", "bf16", "ulysses attention")
-    say(f"  attention {len(rows)} rows: max err O {eo:.3e} LSE {el:.3e}")
+    say(f"  attention out=bf16 {len(rows)} rows: max err O {eo:.3e} LSE {el:.3e}")
     # inverse permute of O back into the sequence-sharded layout (only dst's heads written)
     o_seq = torch.zeros((P, w.batch, s_loc, H, D), dtype=torch.bfloat16, device="cuda")
     ra.head2seq_permute(o, dst, o_seq)
@@ -175,14 +213,13 @@ def test_usp_u4r2_sampled():
     assert torch.equal(got.view(torch.int16), o.view(torch.int16))
 
 
-def test_zigzag_rank3_backward():
-    # The backward at the long zigzag share: dQ of 512 sampled rows against the oracle (each row
-    # needs only its own visible keys), and two identities of the softmax derivative over every
-    # key of every share: rows of P sum to 1 and rows of dS to 0, so per KV head the dK summed
-    # over all keys is 0 and the dV summed over all keys equals dO summed over all queries.
+def _zigzag_bwd_setup(rows):
+    """Inputs of the headline share's backward, the forward run on the GPU, and the stored
+    forward output and LSE of ``rows`` replaced by the oracle's (O rounded to bf16, LSE to fp32):
+    the gradient entries checked against the oracle depend on no other row's forward values."""
     w = synth.get("zigzag_rank3")
     gq, gk, gv = synth.global_qkv(w)
-    n, r, L, H, D = w.world, w.rank, w.global_len, w.heads, w.head_dim
+    n, r, L = w.world, w.rank, w.global_len
     pos = [OP.positions(w.assign, n, s, L) for s in range(n)]
     q_share = np.ascontiguousarray(gq[:, pos[r]])
     do_share = synth.gaussian_bf16_bits(1000 * w.number + 3, q_share.shape)
@@ -190,19 +227,36 @@ def test_zigzag_rank3_backward():
     vd = [dev(np.ascontiguousarray(gv[:, p]), "bf16") for p in pos]
     qd, dod = dev(q_share, "bf16"), dev(do_share, "bf16")
     o, lse = ra.ring_share(qd, kd, vd, r, assign=w.assign)
-    dq, dk, dv = ra.ring_share_bwd(qd, kd, vd, o, lse, dod, r, assign=w.assign)
-    torch.cuda.synchronize()
-    say("zigzag_rank3 backward: kernels done")
-    rows = synth.sample_rows(1000 * w.number, w.share_len, chunk_len=L // (2 * n))
     qpos = pos[r][rows]
     kmax = int(qpos.max()) + 1
-    dq_ref, _, _ = OB.attention_bwd(values(q_share[:, rows], "bf16"), values(gk[:, :kmax], "bf16"),
-                                    values(gv[:, :kmax], "bf16"), values(do_share[:, rows], "bf16"), qpos,
-                                    np.arange(kmax), True)
-    got = host(dq)[:, rows]
-    err = np.abs(got - dq_ref).max() / np.abs(dq_ref).max()
-    say(f"  dQ on {len(rows)} rows x {H} heads: largest error / largest entry {err:.2e}")
-    assert err <= 1e-2
+    ins = (values(q_share[:, rows], "bf16"), values(gk[:, :kmax], "bf16"), values(gv[:, :kmax], "bf16"),
+           values(do_share[:, rows], "bf16"), qpos, np.arange(kmax), True)
+    o_ref, lse_ref = per_head(OA.attention, *ins[:3], qpos, np.arange(kmax), True)
+    o_bits = synth.f32_to_bf16_bits(o_ref.astype(np.float32))
+    ridx = torch.from_numpy(np.asarray(rows)).cuda()
+    o[:, ridx] = dev(o_bits, "bf16")
+    lse[:, :, ridx] = dev(lse_ref.astype(np.float32), "f32")
+    dq, dk, dv = ra.ring_share_bwd(qd, kd, vd, o, lse, dod, r, assign=w.assign)
+    torch.cuda.synchronize()
+    return w, pos, ins, o_ref, o_bits, (dq, dk, dv), do_share
+
+
+@pytest.mark.timeout(600)
+def test_zigzag_rank3_backward():
+    # The backward at the long zigzag share: dQ of 512 sampled rows entry by entry against the
+    # oracle (a row's dQ needs only its own visible keys), and two identities of the softmax
+    # derivative over every key of every share: rows of P sum to 1 and rows of dS to 0, so per KV
+    # head the dK summed over all keys is 0 and the dV summed over all keys equals dO summed over
+    # all queries.
+    w = synth.get("zigzag_rank3")
+    n, L = w.world, w.global_len
+    rows = synth.sample_rows(1000 * w.number, w.share_len, chunk_len=L // (2 * n))
+    w, pos, ins, o_ref, o_bits, (dq, dk, dv), do_share = _zigzag_bwd_setup(rows)
+    say("zigzag_rank3 backward: kernels done")
+    dq_ref, _, _ = per_head(OB.attention_bwd, *ins)
+    mags = per_head(OB.attention_bwd_magnitudes, *ins, delta_err=delta_error(values(o_bits, "bf16"), o_ref, ins[3]))
+    worst = check_grad_entries(host(dq)[:, rows], dq_ref, mags[0], mags[1], "dq sampled rows")
+    say(f"  dQ on {len(rows)} rows x {w.heads} heads: largest error / its entry bound {worst:.2e}")
     dk_sum = sum(host(x).sum(axis=1) for x in dk)          # [B, H_kv, D]
     dk_abs = sum(np.abs(host(x)).sum(axis=1) for x in dk)
     dv_sum = sum(host(x).sum(axis=1) for x in dv)
@@ -212,3 +266,26 @@ def test_zigzag_rank3_backward():
     e_v = np.abs(dv_sum - do_sum).max() / dv_abs.max()
     say(f"  sum over keys: |sum dK| / sum |dK| {e_k:.2e}; |sum dV - sum dO| / sum |dV| {e_v:.2e}")
     assert e_k <= 1e-2 and e_v <= 1e-2
+
+
+@pytest.mark.timeout(600)
+def test_zigzag_rank3_backward_key_gradients():
+    # dK and dV entry by entry at the headline share for the keys whose gradient the oracle can
+    # form from a few query rows: the last 128 keys of the rank's own share (positions
+    # 212864 .. 212991) are seen only by the rank's last 128 queries, which sit at the same
+    # positions. Keys no query of the share sees (the second chunks of shares 0, 1 and 2,
+    # positions 212992 and above) must get gradients of exactly zero.
+    w = synth.get("zigzag_rank3")
+    s, c = w.share_len, w.global_len // (2 * w.world)
+    rows = np.arange(s - 128, s)
+    w, pos, ins, o_ref, o_bits, (dq, dk, dv), _ = _zigzag_bwd_setup(rows)
+    say("zigzag_rank3 backward (key gradients): kernels done")
+    _, dk_ref, dv_ref = per_head(OB.attention_bwd, *ins)
+    mags = per_head(OB.attention_bwd_magnitudes, *ins, delta_err=delta_error(values(o_bits, "bf16"), o_ref, ins[3]))
+    kp = pos[w.rank][rows]                  # the tail keys' positions (equal to the rows')
+    worst = max(check_grad_entries(host(dk[w.rank])[:, rows], dk_ref[:, kp], mags[2][:, kp], mags[3][:, kp], "dk tail"),
+                check_grad_entries(host(dv[w.rank])[:, rows], dv_ref[:, kp], mags[4][:, kp], 0.0, "dv tail"))
+    say(f"  dK/dV of 128 keys x {w.heads} heads: largest error / its entry bound {worst:.2e}")
+    for src in range(w.rank):
+        assert int(pos[src][c:].min()) > int(pos[w.rank].max())
+        assert not torch.any(dk[src][:, c:]) and not torch.any(dv[src][:, c:]), f"share {src}: unseen keys"

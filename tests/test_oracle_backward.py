@@ -69,3 +69,53 @@ def test_delta_is_row_sum_of_p_dp():
     p /= p.sum(axis=-1, keepdims=True)
     dp = np.einsum("bqhd,bkhd->bhqk", do, v)
     assert np.max(np.abs(delta - (p * dp).sum(axis=-1))) < 1e-12
+
+
+def _inputs(seed, b=1, sq=6, sk=9, h=2, h_kv=1, d=5):
+    rng = np.random.default_rng(seed)
+    return (rng.standard_normal((b, sq, h, d)), rng.standard_normal((b, sk, h_kv, d)),
+            rng.standard_normal((b, sk, h_kv, d)), rng.standard_normal((b, sq, h, d)))
+
+
+def test_magnitudes_bound_the_gradients():
+    # triangle inequality: each gradient entry is at most its sum of absolute terms
+    q, k, v, do = _inputs(11)
+    qpos, kpos = np.array([2, 3, 5, 7, 8, 11]), np.arange(9) * 1.5
+    dq, dk, dv = G.attention_bwd(q, k, v, do, qpos, kpos, True)
+    a_dq, e_dq, a_dk, e_dk, a_dv = G.attention_bwd_magnitudes(q, k, v, do, qpos, kpos, True)
+    assert np.all(np.abs(dq) <= a_dq + 1e-12) and np.all(np.abs(dk) <= a_dk + 1e-12)
+    assert np.all(np.abs(dv) <= a_dv + 1e-12)
+    assert not e_dq.any() and not e_dk.any()
+
+
+def test_magnitudes_equal_gradients_for_positive_terms():
+    # with dO >= 0 every term of dV is >= 0, so A_dv == dV; with K >= 0, sum_j P_ij k_j is
+    # attention with V = K, so E_dq / (scale e_i) is that attention's output
+    q, k, v, do = _inputs(12)
+    do, k = np.abs(do), np.abs(k)
+    _, _, dv = G.attention_bwd(q, k, v, do)
+    e = np.full((1, 2, 6), 0.5)
+    _, e_dq, _, _, a_dv = G.attention_bwd_magnitudes(q, k, v, do, delta_err=e)
+    assert np.allclose(a_dv, dv, rtol=1e-13, atol=1e-13)
+    o_kk, _ = A.attention(q, k, k)
+    assert np.allclose(e_dq, o_kk * 0.5 / math.sqrt(5), rtol=1e-13, atol=1e-13)
+
+
+def test_magnitudes_two_key_closed_form():
+    # one query, two visible keys: dS_1 = P1 P2 (dP_1 - dP_2) = -dS_2, so with K all ones
+    # A_dq = scale * 2 P1 P2 |dP_1 - dP_2| in every column
+    rng = np.random.default_rng(13)
+    d = 4
+    q = rng.standard_normal((1, 1, 1, d))
+    k = np.ones((1, 2, 1, d))
+    k[0, 1, 0, 0] = 2.0          # make the two logits differ
+    v = rng.standard_normal((1, 2, 1, d))
+    do = rng.standard_normal((1, 1, 1, d))
+    sc = 1 / math.sqrt(d)
+    s = sc * np.array([q[0, 0, 0] @ k[0, 0, 0], q[0, 0, 0] @ k[0, 1, 0]])
+    p = np.exp(s - s.max())
+    p /= p.sum()
+    dp = np.array([do[0, 0, 0] @ v[0, 0, 0], do[0, 0, 0] @ v[0, 1, 0]])
+    a_dq = G.attention_bwd_magnitudes(q, k, v, do)[0]
+    want = sc * p[0] * p[1] * abs(dp[0] - dp[1]) * (np.abs(k[0, 0, 0]) + np.abs(k[0, 1, 0]))
+    assert np.allclose(a_dq[0, 0, 0], want, rtol=1e-13)

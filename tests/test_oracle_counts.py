@@ -66,3 +66,38 @@ def test_tile_classes_brute():
             blk = mask[i0:i0 + 4, j0:j0 + 8]
             full += blk.all(); skip += (~blk).all(); partial += blk.any() and not blk.all()
     assert C.tile_classes(qpos, kpos, 4, 8) == (full, partial, skip)
+
+
+@pytest.mark.parametrize("assign", ["contiguous", "striped", "zigzag"])
+@pytest.mark.parametrize("n,l", [(1, 40), (2, 64), (4, 200), (3, 96)])
+@pytest.mark.parametrize("causal", [True, False])
+def test_tiled_walk_matches_explicit_masks(assign, n, l, causal):
+    # extreme-position decisions against tile-by-tile explicit masks, ragged tiles included
+    if assign == "zigzag" and l % (2 * n):
+        pytest.skip("zigzag needs L % 2N == 0")
+    for r in range(n):
+        qpos = P.positions(assign, n, r, l)
+        steps = [P.positions(assign, n, (r - s) % n, l) for s in range(n)]
+        for bm, bn, wr in ((8, 4, 2), (12, 5, 4), (16, 16, 16)):
+            got = C.tiled_walk(qpos, steps, bm, bn, wr, causal)
+            want = C.tiled_walk_brute(qpos, steps, bm, bn, wr, causal)
+            assert np.array_equal(got[0], want[0]) and np.array_equal(got[1], want[1]), (r, bm, bn, wr)
+
+
+def test_tiled_walk_totals_are_tile_classes():
+    # visited tiles = full + partial tiles of the same tiling; the skipped ones are the rest
+    n, l = 8, 8192
+    qpos = P.positions("contiguous", n, 7, l)
+    steps = [P.positions("contiguous", n, s, l) for s in range(n)]
+    vis, msk = C.tiled_walk(qpos, steps, 128, 64, 32)
+    full = partial = skip = 0
+    for k in steps:
+        f, p_, s_ = C.tile_classes(qpos, k, 128, 64)
+        full, partial, skip = full + f, partial + p_, skip + s_
+    assert vis.sum() == full + partial and skip == 8 * 8 * 16 - vis.sum()
+    # contiguous rank 7 against itself (shares 0..6 are fully visible): query tile t (rows
+    # 128t .. 128t+127 of the share) visits key tiles 0 .. 2t+1; key tile 2t+1 (keys 128t+64 ..
+    # 128t+127) is partial for all four 32-row blocks, key tile 2t (keys 128t .. 128t+63) for
+    # the first two only
+    assert vis.tolist() == [7 * 16 + 2 * t + 2 for t in range(8)]
+    assert msk.tolist() == [[2, 2, 1, 1]] * 8
