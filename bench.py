@@ -92,8 +92,12 @@ def ring_pairs(w) -> int:
     return sum(ra.share_work(q_sh, ra.Shard(w.assign, n, src, L), s, s, True)[0] for src in range(n))
 
 
+TIMES = {}  # event statistics of the last time_calls of each callable: min, median, mean, count
+
+
 def time_calls(fn, steps, warmup, settle_s=0.0):
-    """(wall ms per call over ``steps`` back-to-back calls, mean event ms per call, median).
+    """(wall ms per call over ``steps`` back-to-back calls, mean event ms per call, median); the
+    minimum, median, mean and count of the per-call events are also left in TIMES[id(fn)].
 
     With ``settle_s`` > 0 (the short secondary workloads) the warm-up goes on for at least that
     many seconds and at least that many seconds are timed: a call of a millisecond or two right
@@ -121,6 +125,7 @@ def time_calls(fn, steps, warmup, settle_s=0.0):
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) * 1e3 / steps
     ev = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    TIMES[id(fn)] = {"min": min(ev), "median": sorted(ev)[len(ev) // 2], "mean": sum(ev) / len(ev), "n": len(ev)}
     return wall, sum(ev) / len(ev), sorted(ev)[len(ev) // 2]
 
 
@@ -137,7 +142,7 @@ def bench_ring(name, steps, warmup, settle_s=0.0):
     flops = 4 * w.head_dim * w.batch * w.heads * ring_pairs(w)
     wall, ev_mean, ev_med = time_calls(call, steps, warmup, settle_s)
     res = {"tflops": flops / (wall * 1e-3) / 1e12, "kernel_ms_mean": ev_mean, "kernel_ms_median": ev_med,
-           "ms_per_step": wall, "flops": flops}
+           "kernel_ms_min": TIMES[id(call)]["min"], "ms_per_step": wall, "flops": flops}
     del inp, o, lse
     torch.cuda.empty_cache()
     return res, host, w
@@ -154,33 +159,39 @@ def bench_ulysses(steps, warmup):
     s_loc = L // P
     stacks = [to_dev(g).view(B, P, s_loc, H, D).transpose(0, 1).contiguous() for g in (gq, gk, gv)]
     del gq, gk, gv
-    # permute bandwidth: rotate the destination rank and the tensor so that successive calls
-    # read different 64 MiB regions (24 distinct sources, 4 output buffers)
-    outs = [torch.empty((B, L, H // P, D), dtype=torch.bfloat16, device="cuda") for _ in range(4)]
-    plan = [(stacks[t], dst) for dst in range(P) for t in range(3)]
+    moved = 2 * B * L * (H // P) * D * 2  # read + write bytes of one tensor's permute
+    # Bandwidth with rotated buffers, so that successive calls read and write different regions
+    # (no Infinity Cache reuse between calls): the destination rank rotates over the 8 head slices
+    # of the three 256 MiB stacks, the outputs over 4 buffers per tensor.
+    outs = [[torch.empty((B, L, H // P, D), dtype=torch.bfloat16, device="cuda") for _ in range(3)] for _ in range(4)]
     idx = [0]
 
-    def perm():
-        x, dst = plan[idx[0] % len(plan)]
-        ra.seq2head_permute(x, dst, out=outs[idx[0] % 4])
+    def perm_one():
+        i = idx[0]
+        ra.seq2head_permute(stacks[i % 3], (i // 3) % P, out=outs[i % 4][i % 3])
+        idx[0] += 1
+
+    def perm_qkv():
+        i = idx[0]
+        ra.seq2head_permute_n(stacks, i % P, outs=outs[i % 4])
         idx[0] += 1
 
     nperm = max(steps, 24)
-    wall, ev_mean, _ = time_calls(perm, nperm, 3, SETTLE_S)
-    moved = 2 * B * L * (H // P) * D * 2  # read + write bytes per call
-    perm_gbs = moved / (ev_mean * 1e-3) / 1e9
-    # context for the HBM roofline: a plain device copy (torch) of the same 64 MiB, same rotation
+    time_calls(perm_one, nperm, 3, SETTLE_S)
+    t_one = TIMES[id(perm_one)]
+    time_calls(perm_qkv, nperm, 3, SETTLE_S)
+    t_qkv = TIMES[id(perm_qkv)]
+    # context for the HBM roofline: a plain device copy (torch) of 64 MiB with the same rotation
     flat = [x.view(-1)[: B * L * (H // P) * D] for x in stacks]
     cidx = [0]
 
     def copy():
-        outs[cidx[0] % 4].view(-1).copy_(flat[cidx[0] % 3])
+        outs[cidx[0] % 4][cidx[0] % 3].view(-1).copy_(flat[cidx[0] % 3])
         cidx[0] += 1
 
     _, ev_copy, _ = time_calls(copy, nperm, 3, SETTLE_S)
-    copy_gbs = moved / (ev_copy * 1e-3) / 1e9
-    # the local step itself: permute Q, K, V for rank 0, causal attention, inverse of O
-    q, k, v = (ra.seq2head_permute(x, w.rank) for x in stacks)
+    # the local step itself: permute Q, K, V for rank 0 (one launch), causal attention, inverse of O
+    q, k, v = ra.seq2head_permute_n(stacks, w.rank)
     full = ra.Shard("contiguous", 1, 0, L)
     o = torch.empty_like(q)
     lse = torch.empty((B, H // P, L), dtype=torch.float32, device="cuda")
@@ -191,15 +202,31 @@ def bench_ulysses(steps, warmup):
     pairs = ra.share_work(full, full, L, L, True)[0]
     flops = 4 * D * B * (H // P) * pairs
     wall_a, ev_a, _ = time_calls(attn, steps, warmup, SETTLE_S)
-    o_seq = torch.empty((P, B, s_loc, H, D), dtype=torch.bfloat16, device="cuda")
-    wall_i, ev_i, _ = time_calls(lambda: ra.head2seq_permute(o, w.rank, o_seq), steps, warmup, SETTLE_S)
-    del stacks, outs, q, k, v, o, lse, o_seq
+    t_attn = TIMES[id(attn)]
+    # inverse permute with rotated sources (12 distinct 64 MiB head-sharded tensors) and targets
+    # (the head slice of dst in one of the three stacks)
+    srcs = [t for grp in outs for t in grp]
+    iidx = [0]
+
+    def inv():
+        i = iidx[0]
+        ra.head2seq_permute(srcs[i % len(srcs)], (i // 3) % P, stacks[i % 3])
+        iidx[0] += 1
+
+    time_calls(inv, nperm, 3, SETTLE_S)
+    t_inv = TIMES[id(inv)]
+    del stacks, outs, q, k, v, o, lse, srcs
     torch.cuda.empty_cache()
-    return {"attention_tflops": flops / (ev_a * 1e-3) / 1e12, "attention_ms": ev_a,
-            "permute_gbs": perm_gbs, "permute_pct_hbm": 100 * perm_gbs / PEAK_HBM_GBS,
-            "device_copy_gbs": copy_gbs,
-            "inverse_permute_gbs": moved / (ev_i * 1e-3) / 1e9,
-            "step_ms": 3 * moved / (perm_gbs * 1e9) * 1e3 + ev_a + ev_i}
+    gbs = lambda ms, nbytes: nbytes / (ms * 1e-3) / 1e9  # noqa: E731
+    return {"attention_tflops": flops / (t_attn["mean"] * 1e-3) / 1e12, "attention_ms": t_attn["mean"],
+            "attention_ms_min": t_attn["min"], "attention_ms_median": t_attn["median"],
+            "permute_gbs": gbs(t_one["mean"], moved), "permute_pct_hbm": 100 * gbs(t_one["mean"], moved) / PEAK_HBM_GBS,
+            "permute_qkv_gbs": gbs(t_qkv["mean"], 3 * moved),
+            "permute_qkv_pct_hbm": 100 * gbs(t_qkv["mean"], 3 * moved) / PEAK_HBM_GBS,
+            "permute_qkv_ms": t_qkv["mean"], "permute_qkv_ms_min": t_qkv["min"],
+            "device_copy_gbs": gbs(ev_copy, moved),
+            "inverse_permute_gbs": gbs(t_inv["mean"], moved), "inverse_permute_ms": t_inv["mean"],
+            "step_ms": t_qkv["mean"] + t_attn["mean"] + t_inv["mean"]}
 
 
 def bench_usp(steps, warmup):
@@ -414,9 +441,54 @@ def cpu_baseline(host, w, budget_s):
             break
     dt = time.perf_counter() - t0
     flops = 4 * w.head_dim * pairs
+    full_pairs = ring_pairs(w) * w.heads * w.batch
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
             "sample": f"{done_rows} sampled query rows x {w.heads} heads of {w.name} ({pairs} visible pairs, "
-                      f"fp64 numpy, {dt:.1f}s incl. bf16->fp64 conversion)"}
+                      f"fp64 numpy, {dt:.1f}s incl. bf16->fp64 conversion)",
+            "cpu_count": os.cpu_count(), "blas_threads": int(cores),
+            "per_row_head_ms": 1e3 * dt / (done_rows * w.heads * w.batch),
+            "full_share_s_extrapolated": dt * full_pairs / pairs}
+
+
+def oracle_configs():
+    """Wall time of the oracle, as it stands, on the other workloads: every row of the tiny exact
+    ring (all four ranks), of the contiguous rank-7 share and of the striped rank-0 share (one
+    OA.attention call each, the share against the whole sequence); for the Ulysses attention,
+    32 sampled rows x its 4 heads, reported per row-head and extrapolated (by visible pairs) to
+    the full attention. The headline share's figures are in the cpu_baseline entry."""
+    import numpy as np
+
+    import synth
+    from oracle import attention as OA
+    from oracle import positions as OP
+    out = {"full_s": {}, "per_row_head_ms": {}, "full_s_extrapolated": {}}
+    for name in ("tiny_exact", "contig_rank7", "striped_rank0"):
+        w = synth.get(name)
+        gq, gk, gv = synth.global_qkv(w)
+        conv = (lambda x: x) if w.dtype == "f32" else synth.bf16_bits_to_f32
+        k, v = conv(gk), conv(gv)
+        ranks = range(w.world) if w.rank < 0 else [w.rank]
+        t0 = time.perf_counter()
+        for r in ranks:
+            qpos = OP.positions(w.assign, w.world, r, w.global_len)
+            OA.attention(conv(np.ascontiguousarray(gq[:, qpos])), k, v, qpos, np.arange(w.global_len), w.causal)
+        out["full_s"][name] = round(time.perf_counter() - t0, 3)
+        log(f"[bench] oracle {name}: {out['full_s'][name]:.1f}s for the whole share")
+    w = synth.get("ulysses_local")
+    gq, gk, gv = synth.global_qkv(w)
+    P, L, H, D = w.world, w.global_len, w.heads, w.head_dim
+    heads = slice(w.rank * H // P, (w.rank + 1) * H // P)   # the destination rank's head slice
+    rows = np.sort(np.random.default_rng(1).choice(L, 32, replace=False))
+    kmax = int(rows.max()) + 1
+    t0 = time.perf_counter()
+    OA.attention(synth.bf16_bits_to_f32(np.ascontiguousarray(gq[:, rows, heads])),
+                 synth.bf16_bits_to_f32(np.ascontiguousarray(gk[:, :kmax, heads])),
+                 synth.bf16_bits_to_f32(np.ascontiguousarray(gv[:, :kmax, heads])), rows, np.arange(kmax), True)
+    dt = time.perf_counter() - t0
+    pairs = int((rows + 1).sum()) * (H // P)
+    out["per_row_head_ms"]["ulysses_local"] = round(1e3 * dt / (len(rows) * (H // P)), 3)
+    out["full_s_extrapolated"]["ulysses_local"] = round(dt * (L * (L + 1) // 2) * (H // P) / pairs, 1)
+    return out
 
 
 def traffic_for(kernel_ms_launch):
@@ -441,6 +513,8 @@ def main():
     ap.add_argument("--secondary", default="", help="comma-separated subset of the secondary workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-oracle-configs", action="store_true",
+                    help="skip the oracle wall times of the other workloads (about a minute of host time)")
     args = ap.parse_args()
     every = ("contig_rank7", "striped_rank0", "striped_rank0_std4", "gqa_zigzag_rank3", "ulysses_local", "usp_u4r2",
              "backward_zigzag_rank3", "lse_merge", "striped_vs_contiguous", "tiny_exact")
@@ -465,7 +539,8 @@ def main():
     achieved = head["flops"] / (head["kernel_ms_mean"] * 1e-3) / 1e12
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic_for(head["kernel_ms_mean"]),
-                "kernel": "attn_bf16_kernel<128, OutBf16, 1, 0>", "kernel_ms": round(head["kernel_ms_mean"], 4),
+                "kernel": "attn_bf16_kernel<128, OutBf16, 1, 0, 0>", "kernel_ms": round(head["kernel_ms_mean"], 4),
+                "kernel_ms_min": round(head["kernel_ms_min"], 4), "kernel_ms_median": round(head["kernel_ms_median"], 4),
                 "flops_per_launch": head["flops"]}
 
     secondary = {}
@@ -473,7 +548,8 @@ def main():
         for name in [n for n in every[:4] if n in chosen]:
             r, _, _ = bench_ring(name, args.steps, args.warmup, SETTLE_S)
             secondary[name] = {"tflops": round(r["tflops"], 2), "pct_bf16_peak": round(100 * r["tflops"] / PEAK_BF16_TFLOPS, 2),
-                               "kernel_ms": round(r["kernel_ms_mean"], 4)}
+                               "kernel_ms": round(r["kernel_ms_mean"], 4), "kernel_ms_min": round(r["kernel_ms_min"], 4),
+                               "kernel_ms_median": round(r["kernel_ms_median"], 4)}
             log(f"[bench] {name}: {r['tflops']:.1f} TFLOP/s")
         if "ulysses_local" in chosen:
             u = bench_ulysses(args.steps, args.warmup)
@@ -510,6 +586,8 @@ def main():
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(host, w, args.cpu_seconds)
         log(f"[bench] cpu_baseline: {cpu['value']:.4f} TFLOP/s on {cpu['cores']} threads")
+        if not args.no_oracle_configs:
+            cpu["oracle_configs"] = oracle_configs()
 
     line = {"metric": METRIC, "value": round(head["tflops"], 2), "unit": "TFLOP/s", "n_gpus": 1,
             "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(head["ms_per_step"], 4),

@@ -59,6 +59,7 @@ extern "C" {
 #define RA_ERR_HIP (-5)          /* a HIP launch error */
 
 #define RA_MAX_WORLD 64          /* largest ring size N accepted by ra_ring_share */
+#define RA_MAX_PERMUTE 8         /* most tensors one ra_seq2head_permute_n call moves */
 
 typedef enum { RA_F32 = 0, RA_BF16 = 1 } ra_dtype;
 
@@ -211,6 +212,17 @@ int ra_ring_share_bwd(const void* q, const void* const* k_shares, const void* co
 int ra_seq2head_permute(const void* in, void* out, int64_t B, int64_t P, int64_t S_loc,
                         int64_t H, int64_t D, int dtype, int dst_rank, int inverse,
                         hipStream_t stream);
+
+/*
+ * ra_seq2head_permute_n -- ra_seq2head_permute of n_tensors tensors of the same shape and dtype
+ * in one launch (the Q, K and V of a Ulysses step: [Digest] §5.1 sends all three through the
+ * all-to-all). ins / outs are HOST arrays of n_tensors device pointers; tensor i is permuted from
+ * ins[i] into outs[i] exactly as ra_seq2head_permute(ins[i], outs[i], ...) would. 0 <= n_tensors
+ * <= RA_MAX_PERMUTE (else RA_ERR_INVALID_ARG); other arguments and errors as ra_seq2head_permute.
+ */
+int ra_seq2head_permute_n(const void* const* ins, void* const* outs, int n_tensors, int64_t B,
+                          int64_t P, int64_t S_loc, int64_t H, int64_t D, int dtype, int dst_rank,
+                          int inverse, hipStream_t stream);
 
 /* Thread-local description of the last failure on this thread ("" after success). */
 const char* ra_last_error(void);

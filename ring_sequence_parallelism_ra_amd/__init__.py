@@ -8,6 +8,7 @@ the thin ctypes binding over it. Importing fails if the library has not been bui
 """
 from ._lib import (ASSIGN, BF16, CONTIGUOUS, EXPORTS, F32, LIB_PATH, STRIPED, ZIGZAG, RaError,  # noqa: F401
                    Shard, last_error, lib)
-from .api import (block_attn_fwd, debug_mask, debug_positions, head2seq_permute, lse_merge,  # noqa: F401
-                  prepare_ring_share, ring_share, ring_share_bwd, ring_share_workspace, ring_share_workspace_bytes,
-                  seq2head_permute, share_work, tile_shape, torch_dtype, usp_local_step)
+from .api import (block_attn_fwd, debug_mask, debug_positions, debug_tile_counts, head2seq_permute,  # noqa: F401
+                  lse_merge, prepare_ring_share, ring_share, ring_share_bwd, ring_share_workspace,
+                  ring_share_workspace_bytes, seq2head_permute, seq2head_permute_n, share_work, tile_shape,
+                  torch_dtype, usp_local_step)

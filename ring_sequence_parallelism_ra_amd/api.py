@@ -238,6 +238,43 @@ def seq2head_permute(x, dst_rank, out=None, stream=None):
     return out
 
 
+def seq2head_permute_n(xs, dst_rank, outs=None, inverse=False, stream=None):
+    """ra_seq2head_permute_n: the permute (or, with ``inverse``, its inverse) of several tensors of
+    one shape and dtype in one launch. Forward: xs are [P, B, S_loc, H, D] stacks, outs (allocated
+    when None) their head-sharded results. Inverse: xs are head-sharded tensors, outs the
+    [P, B, S_loc, H, D] stacks to write (only dst_rank's heads are written)."""
+    xs = list(xs)
+    if not xs:
+        return []
+    if outs is None:
+        if inverse:
+            raise ValueError("the inverse writes into caller-supplied outs")
+        p, b, s, h, d = xs[0].shape
+        shape = (b, p * s, h // p, d) if dst_rank >= 0 else (p, b, p * s, h // p, d)
+        outs = [torch.empty(shape, dtype=xs[0].dtype, device=xs[0].device) for _ in xs]
+    outs = list(outs)
+    if len(outs) != len(xs):
+        raise ValueError("xs and outs differ in length")
+    seq = outs if inverse else xs
+    p, b, s, h, d = seq[0].shape
+    _expect(seq[0], "stack", seq[0].shape, tuple(_DT))
+    if h % p:
+        raise ValueError(f"P={p} does not divide H={h}")
+    head_shape = (b, p * s, h // p, d) if dst_rank >= 0 else (p, b, p * s, h // p, d)
+    for i, (x, y) in enumerate(zip(xs, outs)):
+        src_shape, dst_shape = ((head_shape, (p, b, s, h, d)) if inverse else ((p, b, s, h, d), head_shape))
+        _expect(x, f"xs[{i}]", src_shape, seq[0].dtype)
+        _expect(y, f"outs[{i}]", dst_shape, seq[0].dtype)
+        _need(x, f"xs[{i}]")
+        _need(y, f"outs[{i}]")
+    n = len(xs)
+    ip = (ctypes.c_void_p * n)(*[t.data_ptr() for t in xs])
+    op = (ctypes.c_void_p * n)(*[t.data_ptr() for t in outs])
+    check(lib.ra_seq2head_permute_n(ip, op, n, b, p, s, h, d, _dt(seq[0]), dst_rank, 1 if inverse else 0,
+                                    _stream(stream)))
+    return outs
+
+
 def head2seq_permute(y, dst_rank, out, stream=None):
     """Inverse: write y (dst_rank's head-sharded tensor, or the stack) back into
     out [P, B, S_loc, H, D], touching only dst_rank's heads (all for -1)."""

@@ -106,6 +106,9 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(void* __restrict__ o_acc
 // Sequence-sharded [P, B, S, H, D] <-> head-sharded [B, P*S, H/P, D] (per destination rank).
 // A "row" is one (src, b, s) position: its destination-rank slice is Hp*D contiguous
 // elements on both sides. VEC = bytes moved per access (16 when rows and offsets allow).
+// One launch moves up to kMaxPermute tensors of the same shape (blockIdx.y picks the tensor),
+// so the Q, K and V of a Ulysses step go in one grid. IDX is the index type: 32-bit when every
+// offset of a tensor fits (cheap division), 64-bit otherwise.
 template <int VEC>
 struct VecT;
 template <>
@@ -115,28 +118,36 @@ struct VecT<4> { typedef uint32_t type; };
 template <>
 struct VecT<2> { typedef uint16_t type; };
 
-template <int VEC>
-__global__ __launch_bounds__(256) void permute_kernel(const char* __restrict__ in, char* __restrict__ out,
-                                                      int64_t B, int64_t P, int64_t S, int64_t H,
-                                                      int64_t row_bytes, int64_t in_row_bytes,
-                                                      int64_t first_rank, int64_t n_ranks, int inverse) {
+struct PermuteArgs {
+  const char* in[kMaxPermute];
+  char* out[kMaxPermute];
+};
+
+template <int VEC, typename IDX>
+__global__ __launch_bounds__(256) void permute_kernel(const PermuteArgs t, IDX B, IDX P, IDX S,
+                                                      IDX row_bytes, IDX in_row_bytes, IDX first_rank,
+                                                      IDX n_ranks, int inverse) {
   typedef typename VecT<VEC>::type vec_t;
-  const int64_t per_row = row_bytes / VEC;
-  const int64_t rows = P * B * S;
-  const int64_t n = per_row * rows * n_ranks;
-  for (int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; u < n; u += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t c = u % per_row;
-    const int64_t r = u / per_row;
-    const int64_t row = r % rows;      // index over (b, src, s) in head-sharded order
-    const int64_t k = r / rows;        // which destination rank of the batch
-    const int64_t dst = first_rank + k;
-    const int64_t s = row % S;
-    const int64_t src = (row / S) % P;
-    const int64_t b = row / (S * P);
+  const char* __restrict__ in = t.in[blockIdx.y];
+  char* __restrict__ out = t.out[blockIdx.y];
+  const IDX per_row = row_bytes / VEC;
+  const IDX rows = P * B * S;
+  const IDX n = per_row * rows * n_ranks;
+  const IDX stride = (IDX)gridDim.x * blockDim.x;
+  for (IDX u = (IDX)blockIdx.x * blockDim.x + threadIdx.x; u < n; u += stride) {
+    const IDX r = u / per_row;
+    const IDX c = u - r * per_row;
+    const IDX k = r / rows;            // which destination rank of the batch
+    const IDX row = r - k * rows;      // index over (b, src, s) in head-sharded order
+    const IDX bsrc = row / S;
+    const IDX s = row - bsrc * S;
+    const IDX b = bsrc / P;
+    const IDX src = bsrc - b * P;
+    const IDX dst = first_rank + k;
     // sequence-sharded side: [P, B, S, H*D], slice of rank dst
-    const int64_t seq_off = ((src * B + b) * S + s) * in_row_bytes + dst * row_bytes + c * VEC;
-    // head-sharded side: [n_ranks, B, P*S, Hp*D]
-    const int64_t head_off = ((k * B + b) * (P * S) + src * S + s) * row_bytes + c * VEC;
+    const IDX seq_off = ((src * B + b) * S + s) * in_row_bytes + dst * row_bytes + c * VEC;
+    // head-sharded side: [n_ranks, B, P*S, Hp*D] (consecutive u: consecutive bytes)
+    const IDX head_off = r * row_bytes + c * VEC;
     if (!inverse) {
       *(vec_t*)(out + head_off) = *(const vec_t*)(in + seq_off);
     } else {
@@ -176,27 +187,47 @@ hipError_t launch_lse_merge(void* o_acc, float* lse_acc, const void* o_blk, cons
   return hipGetLastError();
 }
 
-hipError_t launch_permute(const void* in, void* out, int64_t B, int64_t P, int64_t S_loc,
-                          int64_t H, int64_t D, int esize, int dst_rank, int inverse,
-                          hipStream_t stream) {
+template <int VEC, typename IDX>
+static void launch_permute_t(const PermuteArgs& t, int n_t, int64_t B, int64_t P, int64_t S_loc, int64_t row_bytes,
+                             int64_t in_row_bytes, int64_t first, int64_t nr, int inverse, hipStream_t stream) {
+  const int64_t n = row_bytes * P * B * S_loc * nr / VEC;
+  const int64_t blocks = (n + 255) / 256;
+  const dim3 blk(256), g((unsigned)(blocks < 1048576 ? blocks : 1048576), (unsigned)n_t);
+  hipLaunchKernelGGL((permute_kernel<VEC, IDX>), g, blk, 0, stream, t, (IDX)B, (IDX)P, (IDX)S_loc, (IDX)row_bytes,
+                     (IDX)in_row_bytes, (IDX)first, (IDX)nr, inverse);
+}
+
+template <typename IDX>
+static void launch_permute_v(int vec, const PermuteArgs& t, int n_t, int64_t B, int64_t P, int64_t S_loc,
+                             int64_t row_bytes, int64_t in_row_bytes, int64_t first, int64_t nr, int inverse,
+                             hipStream_t stream) {
+  if (vec == 16) launch_permute_t<16, IDX>(t, n_t, B, P, S_loc, row_bytes, in_row_bytes, first, nr, inverse, stream);
+  else if (vec == 4) launch_permute_t<4, IDX>(t, n_t, B, P, S_loc, row_bytes, in_row_bytes, first, nr, inverse, stream);
+  else launch_permute_t<2, IDX>(t, n_t, B, P, S_loc, row_bytes, in_row_bytes, first, nr, inverse, stream);
+}
+
+hipError_t launch_permute(const void* const* in, void* const* out, int n_t, int64_t B, int64_t P, int64_t S_loc,
+                          int64_t H, int64_t D, int esize, int dst_rank, int inverse, hipStream_t stream) {
   const int64_t hp = H / P;
   const int64_t row_bytes = hp * D * esize;
   const int64_t in_row_bytes = H * D * esize;
   const int64_t first = dst_rank < 0 ? 0 : dst_rank;
   const int64_t nr = dst_rank < 0 ? P : 1;
   const int64_t total = row_bytes * P * B * S_loc * nr;
-  if (total == 0) return hipSuccess;
-  const bool v16 = row_bytes % 16 == 0 && (((uintptr_t)in | (uintptr_t)out) % 16) == 0;
+  if (total == 0 || n_t == 0) return hipSuccess;
+  PermuteArgs t;
+  uintptr_t any = 0;
+  for (int i = 0; i < kMaxPermute; ++i) {
+    t.in[i] = i < n_t ? (const char*)in[i] : nullptr;
+    t.out[i] = i < n_t ? (char*)out[i] : nullptr;
+    if (i < n_t) any |= (uintptr_t)in[i] | (uintptr_t)out[i];
+  }
+  const bool v16 = row_bytes % 16 == 0 && any % 16 == 0;
   const int vec = v16 ? 16 : (row_bytes % 4 == 0 ? 4 : 2);
-  const int64_t n = total / vec;
-  const int64_t blocks = (n + 255) / 256;
-  const dim3 blk(256), g((unsigned)(blocks < 1048576 ? blocks : 1048576));
-  if (vec == 16)
-    hipLaunchKernelGGL((permute_kernel<16>), g, blk, 0, stream, (const char*)in, (char*)out, B, P, S_loc, H, row_bytes, in_row_bytes, first, nr, inverse);
-  else if (vec == 4)
-    hipLaunchKernelGGL((permute_kernel<4>), g, blk, 0, stream, (const char*)in, (char*)out, B, P, S_loc, H, row_bytes, in_row_bytes, first, nr, inverse);
-  else
-    hipLaunchKernelGGL((permute_kernel<2>), g, blk, 0, stream, (const char*)in, (char*)out, B, P, S_loc, H, row_bytes, in_row_bytes, first, nr, inverse);
+  // every byte offset of one tensor (both sides span P*B*S_loc*H*D elements) below 2^31
+  const bool small = P * B * S_loc * H * D * esize < ((int64_t)1 << 31);
+  if (small) launch_permute_v<uint32_t>(vec, t, n_t, B, P, S_loc, row_bytes, in_row_bytes, first, nr, inverse, stream);
+  else launch_permute_v<uint64_t>(vec, t, n_t, B, P, S_loc, row_bytes, in_row_bytes, first, nr, inverse, stream);
   return hipGetLastError();
 }
 

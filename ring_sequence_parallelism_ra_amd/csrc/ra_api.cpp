@@ -438,21 +438,35 @@ int ra_lse_merge(void* o_acc, float* lse_acc, const void* o_blk, const float* ls
   return ok();
 }
 
-int ra_seq2head_permute(const void* in, void* out, int64_t B, int64_t P, int64_t S_loc, int64_t H,
-                        int64_t D, int dtype, int dst_rank, int inverse, hipStream_t stream) {
+int ra_seq2head_permute_n(const void* const* ins, void* const* outs, int n_tensors, int64_t B, int64_t P,
+                          int64_t S_loc, int64_t H, int64_t D, int dtype, int dst_rank, int inverse,
+                          hipStream_t stream) {
   if (B < 0 || S_loc < 0 || H < 0 || D < 0) return fail(RA_ERR_INVALID_ARG, "negative size");
   if (P < 1) return fail(RA_ERR_INVALID_ARG, "P=%lld < 1", (long long)P);
+  if (n_tensors < 0 || n_tensors > RA_MAX_PERMUTE)
+    return fail(RA_ERR_INVALID_ARG, "n_tensors=%d not in [0, %d]", n_tensors, RA_MAX_PERMUTE);
   if (!dtype_ok(dtype)) return fail(RA_ERR_UNSUPPORTED, "dtype %d not RA_F32/RA_BF16", dtype);
   if (H % P) return fail(RA_ERR_SHAPE, "P=%lld does not divide H=%lld", (long long)P, (long long)H);
   if (dst_rank < -1 || dst_rank >= P)
     return fail(RA_ERR_INVALID_ARG, "dst_rank %d not in [-1, %lld)", dst_rank, (long long)P);
-  if (B * S_loc * H * D == 0) return ok();
-  if (!in || !out) return fail(RA_ERR_INVALID_ARG, "NULL tensor pointer");
-  if (misaligned(in) || misaligned(out)) return fail(RA_ERR_MISALIGNED, "tensor pointer not 16-byte aligned");
-  hipError_t e = ra::launch_permute(in, out, B, P, S_loc, H, D, dtype == RA_BF16 ? 2 : 4, dst_rank,
+  if (B * S_loc * H * D == 0 || n_tensors == 0) return ok();
+  if (!ins || !outs) return fail(RA_ERR_INVALID_ARG, "NULL tensor array");
+  for (int i = 0; i < n_tensors; ++i) {
+    if (!ins[i] || !outs[i]) return fail(RA_ERR_INVALID_ARG, "tensor %d pointer is NULL", i);
+    if (misaligned(ins[i]) || misaligned(outs[i]))
+      return fail(RA_ERR_MISALIGNED, "tensor %d pointer not 16-byte aligned", i);
+  }
+  hipError_t e = ra::launch_permute(ins, outs, n_tensors, B, P, S_loc, H, D, dtype == RA_BF16 ? 2 : 4, dst_rank,
                                     inverse ? 1 : 0, stream);
   if (e != hipSuccess) return fail(RA_ERR_HIP, "permute launch failed: %s", hipGetErrorString(e));
   return ok();
+}
+
+int ra_seq2head_permute(const void* in, void* out, int64_t B, int64_t P, int64_t S_loc, int64_t H,
+                        int64_t D, int dtype, int dst_rank, int inverse, hipStream_t stream) {
+  const void* ins[1] = {in};
+  void* outs[1] = {out};
+  return ra_seq2head_permute_n(ins, outs, 1, B, P, S_loc, H, D, dtype, dst_rank, inverse, stream);
 }
 
 int ra_share_work(const ra_shard* q_sh, const ra_shard* kv_sh, int64_t Sq, int64_t Sk, int causal,

@@ -125,9 +125,9 @@ hipError_t launch_attn_f32(const AttnArgs& a, int D, int o_dtype, hipStream_t st
 hipError_t launch_lse_merge(void* o_acc, float* lse_acc, const void* o_blk, const float* lse_blk,
                             int64_t B, int64_t H, int64_t S, int64_t D, int acc_dtype,
                             int blk_dtype, hipStream_t stream);
-hipError_t launch_permute(const void* in, void* out, int64_t B, int64_t P, int64_t S_loc,
-                          int64_t H, int64_t D, int esize, int dst_rank, int inverse,
-                          hipStream_t stream);
+constexpr int kMaxPermute = RA_MAX_PERMUTE;  // tensors one permute launch moves
+hipError_t launch_permute(const void* const* in, void* const* out, int n_t, int64_t B, int64_t P, int64_t S_loc,
+                          int64_t H, int64_t D, int esize, int dst_rank, int inverse, hipStream_t stream);
 hipError_t launch_debug_positions(Pos p, int64_t n, int64_t* out, hipStream_t stream);
 hipError_t launch_debug_mask(Pos q, Pos kv, int64_t Sq, int64_t Sk, uint8_t* out,
                              hipStream_t stream);

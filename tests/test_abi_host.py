@@ -163,6 +163,19 @@ def test_permute_validation():
     assert f(None, None, 1, 4, 0, 8, 128, 1, 0, 0, None) == OK              # empty
 
 
+def test_permute_n_validation():
+    f = lib.ra_seq2head_permute_n
+    arr = (ctypes.c_void_p * 3)(0x10000, 0x10000, 0x10000)
+    assert f(arr, arr, 9, 1, 4, 8, 8, 128, 1, 0, 0, None) == INVALID     # more than RA_MAX_PERMUTE
+    assert f(arr, arr, -1, 1, 4, 8, 8, 128, 1, 0, 0, None) == INVALID
+    assert f(arr, arr, 3, 1, 4, 8, 6, 128, 1, 0, 0, None) == SHAPE       # 4 does not divide 6
+    nulls = (ctypes.c_void_p * 3)(0x10000, 0, 0x10000)
+    assert f(arr, nulls, 3, 1, 4, 8, 8, 128, 1, 0, 0, None) == INVALID
+    mis = (ctypes.c_void_p * 3)(0x10000, 0x10000, 0x10008)
+    assert f(mis, arr, 3, 1, 4, 8, 8, 128, 1, 0, 0, None) == MISALIGNED
+    assert f(None, None, 0, 1, 4, 8, 8, 128, 1, 0, 0, None) == OK         # nothing to move
+
+
 def test_merge_validation():
     f = lib.ra_lse_merge
     assert f(FAKE, FAKE, FAKE, FAKE, 1, 2, 4, 12, 1, 1, None) == UNSUP      # D % 8

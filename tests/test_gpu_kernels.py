@@ -486,6 +486,29 @@ def test_permute_bit_exact(p, hmul, s, d, dt):
         assert np.array_equal(got_back, want_back.view(np.int16 if dt == "bf16" else np.int32))
 
 
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("p,hmul,s,d,nt", [(8, 1, 64, 128, 3), (4, 2, 3, 64, 2), (2, 3, 5, 1, 8), (8, 4, 17, 8, 1)])
+def test_permute_n_bit_exact(p, hmul, s, d, nt, dt):
+    # several tensors in one launch, each exactly as the one-tensor permute (and the oracle)
+    h, b = p * hmul, 2
+    xs = [gen(760 + i, (p, b, s, h, d), dt) for i in range(nt)]
+    xd = [dev(x, dt) for x in xs]
+    iv = torch.int16 if dt == "bf16" else torch.int32
+    nv = np.int16 if dt == "bf16" else np.int32
+    for dst in (p - 1, -1):
+        ys = ra.seq2head_permute_n(xd, dst)
+        torch.cuda.synchronize()
+        for x, y in zip(xs, ys):
+            assert np.array_equal(y.cpu().view(iv).numpy(), OU.seq2head(x, dst).view(nv))
+        fills = [np.full_like(x, 0x3f80 if dt == "bf16" else 7) for x in xs]
+        outs = [dev(f, dt) for f in fills]
+        ra.seq2head_permute_n(ys, dst, outs, inverse=True)
+        torch.cuda.synchronize()
+        for f, x, o in zip(fills, xs, outs):
+            want = OU.head2seq(OU.seq2head(x, dst), dst, f.copy())
+            assert np.array_equal(o.cpu().view(iv).numpy(), want.view(nv))
+
+
 def test_future_keys_never_read():
     # Keys later than every query of the share are invisible: filling them with +-1e4 garbage
     # must leave O and LSE bit-identical (tile skipping and masking together).
