@@ -60,6 +60,7 @@ extern "C" {
 
 #define RA_MAX_WORLD 64          /* largest ring size N accepted by ra_ring_share */
 #define RA_MAX_PERMUTE 8         /* most tensors one ra_seq2head_permute_n call moves */
+#define RA_BWD_NOALLOC_MAX_BYTES (16 << 20)  /* device scratch of ra_ring_share_bwd_noalloc */
 
 typedef enum { RA_F32 = 0, RA_BF16 = 1 } ra_dtype;
 
@@ -193,6 +194,23 @@ int ra_ring_share_bwd(const void* q, const void* const* k_shares, const void* co
                       int64_t H_kv, int64_t S_loc, int64_t D, int N, int rank, int assign,
                       int causal, int in_dtype, float scale, void* ws, size_t ws_bytes,
                       hipStream_t stream);
+
+/*
+ * ra_ring_share_bwd_noalloc -- ra_ring_share_bwd for callers that cannot allocate device memory
+ * (code being captured into a HIP graph, tight serving loops, harnesses that forbid hipMalloc):
+ * the same arguments without ws / ws_bytes, the same kernels and the same results. The row terms
+ * Delta live in a static device array of RA_BWD_NOALLOC_MAX_BYTES (16 MiB) that the library holds
+ * on every device it runs on until the process ends; the call allocates and frees nothing.
+ * Limit: 4 * B * H * S_loc <= RA_BWD_NOALLOC_MAX_BYTES, else RA_ERR_UNSUPPORTED (before anything
+ * is launched). Every call on a device uses that device's one array, so calls that overlap on one
+ * device (concurrent streams, or threads without ordering) race and may return wrong gradients;
+ * order them. The array needs no clearing: each call writes every Delta entry before reading it.
+ */
+int ra_ring_share_bwd_noalloc(const void* q, const void* const* k_shares, const void* const* v_shares,
+                              const void* o, const float* lse, const void* dout, float* dq,
+                              float* const* dk_shares, float* const* dv_shares, int64_t B, int64_t H,
+                              int64_t H_kv, int64_t S_loc, int64_t D, int N, int rank, int assign,
+                              int causal, int in_dtype, float scale, hipStream_t stream);
 
 /*
  * ra_seq2head_permute -- the local data movement of the Ulysses all-to-all ([Digest] §5.1,

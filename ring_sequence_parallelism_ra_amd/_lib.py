@@ -28,7 +28,7 @@ STATUS = {0: "RA_OK", -1: "RA_ERR_INVALID_ARG", -2: "RA_ERR_UNSUPPORTED", -3: "R
 
 # Every function the header declares, in declaration order.
 EXPORTS = ["ra_block_attn_fwd", "ra_lse_merge", "ra_ring_share_workspace_bytes", "ra_ring_share",
-           "ra_ring_share_bwd_workspace_bytes", "ra_ring_share_bwd", "ra_seq2head_permute", "ra_seq2head_permute_n", "ra_last_error",
+           "ra_ring_share_bwd_workspace_bytes", "ra_ring_share_bwd", "ra_ring_share_bwd_noalloc", "ra_seq2head_permute", "ra_seq2head_permute_n", "ra_last_error",
            "ra_share_work", "ra_tile_shape", "ra_debug_positions", "ra_debug_mask", "ra_debug_tile_count_slots",
            "ra_debug_tile_counts"]
 
@@ -61,6 +61,7 @@ def _load():
         "ra_ring_share": (I, [P, P, P, P, P, I64, I64, I64, I64, I64, I, I, I, I, I, I, F, I, I, P, SZ, P]),
         "ra_ring_share_bwd_workspace_bytes": (SZ, [I64, I64, I64]),
         "ra_ring_share_bwd": (I, [P, P, P, P, P, P, P, P, P, I64, I64, I64, I64, I64, I, I, I, I, I, F, P, SZ, P]),
+        "ra_ring_share_bwd_noalloc": (I, [P, P, P, P, P, P, P, P, P, I64, I64, I64, I64, I64, I, I, I, I, I, F, P]),
         "ra_seq2head_permute": (I, [P, P, I64, I64, I64, I64, I64, I, I, I, P]),
         "ra_seq2head_permute_n": (I, [P, P, I, I64, I64, I64, I64, I64, I, I, I, P]),
         "ra_last_error": (ctypes.c_char_p, []),

@@ -28,10 +28,18 @@
 // the row so that 128-bit row reads stay conflict-free.
 #include <math.h>
 
+#include <mutex>
+
 #include "ra_internal.h"
 
 namespace ra {
 namespace {
+
+// Row terms Delta of the allocation-free entry point (ra_ring_share_bwd_noalloc): every call
+// on a device uses that device's copy of this array. Host code never passes the array's name
+// to a kernel (on the host it is only a stand-in for the symbol): it passes the device address
+// from bwd_scratch().
+static __device__ __attribute__((aligned(256))) float scratch[RA_BWD_NOALLOC_MAX_BYTES / 4];
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -415,6 +423,25 @@ __global__ __launch_bounds__(NT, RA_DKDV_WG_PER_CU) void dkdv_kernel(const BwdAr
 }
 
 }  // namespace
+
+hipError_t bwd_scratch(float** out) {
+  // The array's device address, looked up once per device (with that device current) and kept.
+  static std::mutex mu;
+  static float* addr[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = (float*)p;
+  }
+  *out = addr[dev];
+  return hipSuccess;
+}
 
 hipError_t launch_attn_bwd(const BwdArgs& a, int D, hipStream_t stream) {
   const int64_t rows = (int64_t)a.B * a.Sq * a.H;

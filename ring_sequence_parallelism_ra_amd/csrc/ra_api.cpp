@@ -354,11 +354,17 @@ size_t ra_ring_share_bwd_workspace_bytes(int64_t B, int64_t H, int64_t S_loc) {
   return (size_t)4 * (size_t)(B * H * S_loc);
 }
 
-int ra_ring_share_bwd(const void* q, const void* const* k_shares, const void* const* v_shares,
-                      const void* o, const float* lse, const void* dout, float* dq,
-                      float* const* dk_shares, float* const* dv_shares, int64_t B, int64_t H,
-                      int64_t H_kv, int64_t S_loc, int64_t D, int N, int rank, int assign, int causal,
-                      int in_dtype, float scale, void* ws, size_t ws_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// ra_ring_share_bwd with the Delta buffer either from the caller's workspace (noalloc == false)
+// or the library's static device scratch (noalloc == true; ws is ignored).
+int ring_share_bwd_impl(const void* q, const void* const* k_shares, const void* const* v_shares,
+                        const void* o, const float* lse, const void* dout, float* dq,
+                        float* const* dk_shares, float* const* dv_shares, int64_t B, int64_t H,
+                        int64_t H_kv, int64_t S_loc, int64_t D, int N, int rank, int assign, int causal,
+                        int in_dtype, float scale, void* ws, size_t ws_bytes, bool noalloc, hipStream_t stream) {
   int rc = check_dims(B, H, S_loc, S_loc, D);
   if (rc) return rc;
   if ((rc = check_kv_heads(H, H_kv))) return rc;
@@ -384,11 +390,22 @@ int ra_ring_share_bwd(const void* q, const void* const* k_shares, const void* co
     if (misaligned(k_shares[i]) || misaligned(v_shares[i]) || misaligned(dk_shares[i]) || misaligned(dv_shares[i]))
       return fail(RA_ERR_MISALIGNED, "share %d pointer not 16-byte aligned", i);
   }
-  if (!ws) return fail(RA_ERR_INVALID_ARG, "workspace needed for the row terms");
-  if (misaligned(ws)) return fail(RA_ERR_MISALIGNED, "workspace not 16-byte aligned");
-  if (ws_bytes < ra_ring_share_bwd_workspace_bytes(B, H, S_loc))
-    return fail(RA_ERR_INVALID_ARG, "workspace %zu bytes < %zu needed", ws_bytes,
-                ra_ring_share_bwd_workspace_bytes(B, H, S_loc));
+  if (noalloc) {
+    if (ra_ring_share_bwd_workspace_bytes(B, H, S_loc) > (size_t)RA_BWD_NOALLOC_MAX_BYTES)
+      return fail(RA_ERR_UNSUPPORTED, "B*H*S_loc = %lld row terms need %zu bytes, above the %d-byte device scratch",
+                  (long long)(B * H * S_loc), ra_ring_share_bwd_workspace_bytes(B, H, S_loc),
+                  RA_BWD_NOALLOC_MAX_BYTES);
+    float* p = nullptr;
+    hipError_t e = ra::bwd_scratch(&p);
+    if (e != hipSuccess) return fail(RA_ERR_HIP, "device scratch lookup failed: %s", hipGetErrorString(e));
+    ws = p;
+  } else {
+    if (!ws) return fail(RA_ERR_INVALID_ARG, "workspace needed for the row terms");
+    if (misaligned(ws)) return fail(RA_ERR_MISALIGNED, "workspace not 16-byte aligned");
+    if (ws_bytes < ra_ring_share_bwd_workspace_bytes(B, H, S_loc))
+      return fail(RA_ERR_INVALID_ARG, "workspace %zu bytes < %zu needed", ws_bytes,
+                  ra_ring_share_bwd_workspace_bytes(B, H, S_loc));
+  }
 
   ra::BwdArgs a;
   memset(&a, 0, sizeof a);
@@ -421,6 +438,28 @@ int ra_ring_share_bwd(const void* q, const void* const* k_shares, const void* co
   hipError_t e = ra::launch_attn_bwd(a, (int)D, stream);
   if (e != hipSuccess) return fail(RA_ERR_HIP, "backward launch failed: %s", hipGetErrorString(e));
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int ra_ring_share_bwd(const void* q, const void* const* k_shares, const void* const* v_shares,
+                      const void* o, const float* lse, const void* dout, float* dq,
+                      float* const* dk_shares, float* const* dv_shares, int64_t B, int64_t H,
+                      int64_t H_kv, int64_t S_loc, int64_t D, int N, int rank, int assign, int causal,
+                      int in_dtype, float scale, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return ring_share_bwd_impl(q, k_shares, v_shares, o, lse, dout, dq, dk_shares, dv_shares, B, H, H_kv, S_loc, D, N,
+                             rank, assign, causal, in_dtype, scale, ws, ws_bytes, false, stream);
+}
+
+int ra_ring_share_bwd_noalloc(const void* q, const void* const* k_shares, const void* const* v_shares,
+                              const void* o, const float* lse, const void* dout, float* dq,
+                              float* const* dk_shares, float* const* dv_shares, int64_t B, int64_t H,
+                              int64_t H_kv, int64_t S_loc, int64_t D, int N, int rank, int assign,
+                              int causal, int in_dtype, float scale, hipStream_t stream) {
+  return ring_share_bwd_impl(q, k_shares, v_shares, o, lse, dout, dq, dk_shares, dv_shares, B, H, H_kv, S_loc, D, N,
+                             rank, assign, causal, in_dtype, scale, nullptr, 0, true, stream);
 }
 
 int ra_lse_merge(void* o_acc, float* lse_acc, const void* o_blk, const float* lse_blk, int64_t B,

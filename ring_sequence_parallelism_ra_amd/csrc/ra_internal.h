@@ -120,6 +120,9 @@ struct BwdArgs {
 
 // Launchers (return hipError_t of the launch).
 hipError_t launch_attn_bwd(const BwdArgs& a, int D, hipStream_t stream);
+constexpr int kMaxDevices = 64;
+// Device address of the backward's static scratch array on the current device.
+hipError_t bwd_scratch(float** out);
 hipError_t launch_attn_bf16(const AttnArgs& a, int D, int o_dtype, hipStream_t stream);
 hipError_t launch_attn_f32(const AttnArgs& a, int D, int o_dtype, hipStream_t stream);
 hipError_t launch_lse_merge(void* o_acc, float* lse_acc, const void* o_blk, const float* lse_blk,

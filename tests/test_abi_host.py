@@ -153,6 +153,22 @@ def test_ring_share_bwd_validation():
     assert call_bwd(B=0, q=None, o=None) == OK            # empty: nothing launched
 
 
+def test_ring_share_bwd_noalloc_validation():
+    # same checks as the workspace form, plus the size of the static device scratch (16 MiB of
+    # fp32 row terms), all on the host
+    f = lib.ra_ring_share_bwd_noalloc
+    arr = (ctypes.c_void_p * 2)(0x10000, 0x10000)
+    args = lambda **o: [o.get(k, v) for k, v in (("q", FAKE), ("ks", arr), ("vs", arr), ("o", FAKE), ("lse", FAKE),
+                                                 ("do", FAKE), ("dq", FAKE), ("dks", arr), ("dvs", arr), ("B", 1),
+                                                 ("H", 64), ("Hkv", 64), ("S", 65536), ("D", 128), ("N", 2), ("rank", 0),
+                                                 ("assign", 0), ("causal", 1), ("ind", 1), ("scale", 0.0), ("st", None))]
+    assert f(*args(S=65536 + 64)) == UNSUP and "scratch" in _lib.last_error()
+    assert f(*args(ind=0)) == UNSUP
+    assert f(*args(rank=2)) == INVALID
+    assert f(*args(dq=ctypes.c_void_p(0x10004))) == MISALIGNED
+    assert f(*args(B=0, q=None)) == OK
+
+
 def test_permute_validation():
     f = lib.ra_seq2head_permute
     assert f(FAKE, FAKE, 1, 4, 8, 6, 128, 1, 0, 0, None) == SHAPE          # 4 does not divide 6
