@@ -100,7 +100,7 @@ typedef struct {
  * in_dtype RA_BF16 runs bf16 MFMA with fp32 accumulation; RA_F32 runs fp32 FMA.
  * D must be 64 or 128. Sq and Sk may be any non-negative size (ragged tails are masked).
  * Global lengths (q_sh->global_len, kv_sh->global_len) must be below 2^31; B*H, Sq and Sk
- * below 2^30; H*D*128 below 2^32 (byte offsets inside a 64-row K/V tile); ceil(Sq/64)*B*H
+ * below 2^30; H*D*2 below 2^24 (bytes of one K/V row, multiplied in 24 bits); ceil(Sq/64)*B*H
  * below 2^31 (the launch grid). Beyond these limits the call returns RA_ERR_UNSUPPORTED.
  */
 int ra_block_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,

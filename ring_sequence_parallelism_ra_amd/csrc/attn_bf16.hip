@@ -88,6 +88,15 @@ constexpr float kLn2 = 0.6931471805599453f;
 #ifndef RA_ATTN_TILE_GROUP
 #define RA_ATTN_TILE_GROUP 32         // consecutive tiles of one step visited before the next step
 #endif
+#ifndef RA_ATTN_MUL24
+#define RA_ATTN_MUL24 1               // 24-bit multiply for the copies' row offsets (rows < 2^24 bytes)
+#endif
+#ifndef RA_ATTN_SOFFSET
+#define RA_ATTN_SOFFSET 1             // the copies' wave-uniform row offset as the scalar offset
+#endif
+#ifndef RA_ATTN_DMA_REGS
+#define RA_ATTN_DMA_REGS 0            // keep the lanes' copy offsets in registers for the whole loop
+#endif
 #ifndef RA_ATTN_WAVES_PER_SIMD
 #define RA_ATTN_WAVES_PER_SIMD 2      // occupancy target: 256 VGPRs per wave at 2, 512 at 1
 #endif

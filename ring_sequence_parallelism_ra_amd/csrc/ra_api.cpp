@@ -63,9 +63,10 @@ int check_dims(int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t D) {
   const int64_t lim = (int64_t)1 << 30;
   if (B * H >= lim || Sq >= lim || Sk >= lim)
     return fail(RA_ERR_UNSUPPORTED, "sizes too large for 32-bit row indexing");
-  // byte offsets inside one 64-row K/V tile (rows of H*D elements) are 32-bit
-  if (H * D * 2 * 64 >= ((int64_t)1 << 32))
-    return fail(RA_ERR_UNSUPPORTED, "H*D=%lld too large for 32-bit tile offsets", (long long)(H * D));
+  // byte offsets inside one 64-row K/V tile (rows of H*D elements) are 32-bit, and the bytes of
+  // one K/V row are multiplied with 24-bit multiplies when the tiles are copied
+  if (H * D * 2 >= ((int64_t)1 << 24))
+    return fail(RA_ERR_UNSUPPORTED, "H*D=%lld: rows of 2^24 bytes or more are not supported", (long long)(H * D));
   // one workgroup per (64-row query tile, batch, head) must fit a 32-bit grid
   if ((Sq + 63) / 64 * B * H >= ((int64_t)1 << 31))
     return fail(RA_ERR_UNSUPPORTED, "launch grid too large");

@@ -174,3 +174,25 @@ def per_head(fn, q, k, v, *rest, delta_err=None, threads=None, **kw):
         xs = [p_[i] for p_ in parts]
         out.append(np.concatenate(xs, axis=2 if xs[0].ndim == 4 else 1))
     return tuple(out)
+
+
+class Guarded:
+    """A device tensor of ``shape`` / ``dtype`` placed between two pads of canary bytes, to
+    catch writes before or after an output (pads of 4 KiB keep the view 16-byte aligned)."""
+    PAD = 4096
+    BYTE = 0xA5
+
+    def __init__(self, shape, dtype, fill=None):
+        esize = torch.tensor([], dtype=dtype).element_size()
+        n = int(np.prod(shape))
+        self.buf = torch.full((2 * self.PAD + n * esize,), self.BYTE, dtype=torch.uint8, device="cuda")
+        self.t = self.buf[self.PAD:self.PAD + n * esize].view(dtype).view(shape)
+        if fill is not None:
+            self.t.copy_(fill)
+
+    def check(self, what=""):
+        torch.cuda.synchronize()
+        head = self.buf[:self.PAD]
+        tail = self.buf[-self.PAD:]
+        assert bool((head == self.BYTE).all()), f"{what}: write before the output"
+        assert bool((tail == self.BYTE).all()), f"{what}: write past the output"

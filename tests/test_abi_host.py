@@ -70,7 +70,9 @@ def test_block_attn_validation():
     assert "divide" in _lib.last_error()
     assert call_block(H=4, Hkv=-1) == INVALID
     # 32-bit limits: byte offsets inside a 64-row K/V tile, and the launch grid
-    assert call_block(H=1 << 18) == UNSUP                 # 2^18 heads x 128 x 2 B x 64 rows = 2^32
+    assert call_block(H=1 << 16) == UNSUP                 # 2^16 heads x 128 x 2 B = 2^24-byte rows
+    assert "2^24" in _lib.last_error()
+    assert call_block(H=(1 << 16) - 8, B=0, q=None, k=None, v=None, o=None, lse=None) == OK
     assert call_block(B=1 << 14, H=1 << 10, Sq=1 << 13, Sk=64) == UNSUP   # 128 x 2^24 workgroups
     assert "grid" in _lib.last_error()
     # causal needs shard descriptors matching the sizes

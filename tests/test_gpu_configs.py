@@ -183,6 +183,41 @@ def test_ulysses_local():
     assert np.array_equal(o_seq.cpu().view(torch.int16).numpy(), back)
 
 
+def test_ulysses_every_rank():
+    # the other seven destination ranks of the Ulysses workload: the permutes of all ranks at once
+    # (bit-exact), each rank's causal attention on its 4 heads (64 seeded rows each, all heads),
+    # and each rank's inverse permute writing only its own heads
+    w = synth.get("ulysses_local")
+    gq, gk, gv = synth.global_qkv(w)
+    P, L, H, D = w.world, w.global_len, w.heads, w.head_dim
+    s_loc, hp = L // P, H // P
+    stack = [np.ascontiguousarray(x.reshape(w.batch, P, s_loc, H, D).transpose(1, 0, 2, 3, 4)) for x in (gq, gk, gv)]
+    every = ra.seq2head_permute_n([dev(x, "bf16") for x in stack], -1)      # [P, B, L, H/P, D] each
+    torch.cuda.synchronize()
+    for got, x in zip(every, stack):
+        assert np.array_equal(got.cpu().view(torch.int16).numpy(), OU.seq2head(x, -1).view(np.int16))
+    say("ulysses: permutes of all 8 ranks bit-exact")
+    full = ra.Shard("contiguous", 1, 0, L)
+    o_seq = torch.zeros((P, w.batch, s_loc, H, D), dtype=torch.bfloat16, device="cuda")
+    rng = np.random.default_rng(1000 * w.number + 11)
+    for p in range(1, P):
+        q, k, v = (t[p] for t in every)
+        o, lse = ra.block_attn_fwd(q, k, v, causal=True, q_shard=full, kv_shard=full)
+        ra.head2seq_permute(o, p, o_seq)
+        torch.cuda.synchronize()
+        rows = np.sort(np.concatenate([[0, L - 1], rng.choice(L, 62, replace=False)]))
+        heads = slice(p * hp, (p + 1) * hp)
+        o_ref, lse_ref = oracle_rows(values(np.ascontiguousarray(gq[:, :, heads]), "bf16"),
+                                     values(np.ascontiguousarray(gk[:, :, heads]), "bf16"),
+                                     values(np.ascontiguousarray(gv[:, :, heads]), "bf16"), rows, rows)
+        eo, el = check(host(o)[:, rows], host(lse)[:, :, rows], o_ref, lse_ref, "bf16", "bf16", f"ulysses rank {p}")
+        say(f"  rank {p}: {len(rows)} rows x {hp} heads: max err O {eo:.3e} LSE {el:.3e}")
+    # every rank but 0 has written its heads back; rank 0's heads are still zero
+    back = o_seq.cpu().view(torch.int16).numpy()
+    assert not back[:, :, :, :hp].any()
+    assert back[:, :, :, hp:].any(axis=(0, 1, 2, 4)).all()
+
+
 def test_usp_u4r2_sampled():
     # one device (Ulysses rank 2 of 4, ring rank 1 of 2) of the 128K-token USP mesh
     w = synth.get("usp_u4r2")
