@@ -164,7 +164,8 @@ int ra_ring_share(const void* q, const void* const* k_shares, const void* const*
                   float scale, int start_step, int num_steps, void* ws, size_t ws_bytes,
                   hipStream_t stream);
 
-/* Bytes of workspace ra_ring_share_bwd needs: the row terms Delta [B, H, S] in fp32. */
+/* Bytes of workspace ra_ring_share_bwd needs: the row terms Delta [B, H, S] and the LSE in log2
+ * units [B, H, S], both fp32. */
 size_t ra_ring_share_bwd_workspace_bytes(int64_t B, int64_t H, int64_t S_loc);
 
 /*
@@ -199,12 +200,13 @@ int ra_ring_share_bwd(const void* q, const void* const* k_shares, const void* co
  * ra_ring_share_bwd_noalloc -- ra_ring_share_bwd for callers that cannot allocate device memory
  * (code being captured into a HIP graph, tight serving loops, harnesses that forbid hipMalloc):
  * the same arguments without ws / ws_bytes, the same kernels and the same results. The row terms
- * Delta live in a static device array of RA_BWD_NOALLOC_MAX_BYTES (16 MiB) that the library holds
- * on every device it runs on until the process ends; the call allocates and frees nothing.
- * Limit: 4 * B * H * S_loc <= RA_BWD_NOALLOC_MAX_BYTES, else RA_ERR_UNSUPPORTED (before anything
- * is launched). Every call on a device uses that device's one array, so calls that overlap on one
+ * (what ra_ring_share_bwd keeps in its workspace) live in a static device array of
+ * RA_BWD_NOALLOC_MAX_BYTES (16 MiB) that the library holds on every device it runs on until the
+ * process ends; the call allocates and frees nothing. Limit:
+ * ra_ring_share_bwd_workspace_bytes(B, H, S_loc) = 8 * B * H * S_loc <= RA_BWD_NOALLOC_MAX_BYTES,
+ * i.e. B * H * S_loc <= 2,097,152, else RA_ERR_UNSUPPORTED (before anything is launched). Every call on a device uses that device's one array, so calls that overlap on one
  * device (concurrent streams, or threads without ordering) race and may return wrong gradients;
- * order them. The array needs no clearing: each call writes every Delta entry before reading it.
+ * order them. The array needs no clearing: each call writes every row term before reading it.
  */
 int ra_ring_share_bwd_noalloc(const void* q, const void* const* k_shares, const void* const* v_shares,
                               const void* o, const float* lse, const void* dout, float* dq,

@@ -10,7 +10,7 @@
 //     dQ = scale dS K,   dK = scale dS^T Q,       dV = P^T dO.
 //
 // Three launches, bf16 inputs, fp32 gradients:
-//  * delta_kernel   Delta [B, H, S] = sum over d of O * dO (HBM-bound);
+//  * delta_kernel   Delta [B, H, S] = sum over d of O * dO, and the LSE in log2 units (HBM-bound);
 //  * dq_kernel      query-stationary like the forward: a workgroup of 4 wave64s owns 128
 //                   query rows of one (batch, head) and walks the visible K/V tiles of every
 //                   step; per 64-key tile it forms S^T = K Q^T and dP^T = V dO^T with
@@ -35,7 +35,7 @@
 namespace ra {
 namespace {
 
-// Row terms Delta of the allocation-free entry point (ra_ring_share_bwd_noalloc): every call
+// Row terms (Delta, then the log2 LSE) of the allocation-free entry point (ra_ring_share_bwd_noalloc): every call
 // on a device uses that device's copy of this array. Host code never passes the array's name
 // to a kernel (on the host it is only a stand-in for the symbol): it passes the device address
 // from bwd_scratch().
@@ -91,12 +91,13 @@ __device__ inline void copy_tile(__amdgpu_buffer_rsrc_t r, __bf16* tile, uint32_
   using L = Lay<D>;
   int lr = lane / L::SPR, lc = lane % L::SPR;
   asm volatile("" : "+v"(lr), "+v"(lc));  // formed at each copy: kept live they would cost registers
+  const uint32_t lb = __umul24((uint32_t)lr, rowb);  // rows are below 2^24 bytes (checked on the host)
 #pragma unroll
   for (int i = 0; i < L::DMA; ++i) {
-    const int row = (wave * L::DMA + i) * L::RPC + lr;
-    const uint32_t off = (uint32_t)row * rowb + (uint32_t)((lc ^ L::swz(row)) * 16);
+    const int row0 = (wave * L::DMA + i) * L::RPC;  // wave-uniform: the copy's scalar offset
+    const uint32_t off = lb + (uint32_t)((lc ^ L::swz(row0 + lr)) * 16);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(tile + (wave * L::DMA + i) * 512),
-                                             16, off, 0, 0, 0);
+                                             16, off, (uint32_t)row0 * rowb, 0, 0);
   }
 }
 
@@ -139,8 +140,11 @@ __device__ inline bf16x8 read_r(const __bf16* tile, const Offsets<D>& of, int ks
   return *(const bf16x8*)((const char*)tile + r0 * Lay<D>::ROWB + of.row[ks]);
 }
 
+// Also stores the LSE in log2 units (lse2 = LSE * log2 e; +inf for a row with no visible key,
+// so that its weights come out 0), the form the dK/dV kernel takes its weights against.
 __global__ __launch_bounds__(256) void delta_kernel(const __bf16* __restrict__ o, const __bf16* __restrict__ dout,
-                                                    float* __restrict__ delta, int64_t B, int64_t S, int64_t H,
+                                                    const float* __restrict__ lse, float* __restrict__ delta,
+                                                    float* __restrict__ lse2, int64_t B, int64_t S, int64_t H,
                                                     int D) {
   const int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // (b, s, h) row
   if (u >= B * S * H) return;
@@ -153,7 +157,10 @@ __global__ __launch_bounds__(256) void delta_kernel(const __bf16* __restrict__ o
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc = fmaf((float)x[e], (float)y[e], acc);
   }
-  delta[(b * H + h) * S + s] = acc;
+  const int64_t r = (b * H + h) * S + s;
+  delta[r] = acc;
+  const float ln = lse[r];
+  lse2[r] = ln == -INFINITY ? INFINITY : ln * kLog2e;
 }
 
 template <int D>
@@ -245,17 +252,26 @@ __global__ __launch_bounds__(NT, 2) void dq_kernel(const BwdArgs a) {
         const int key0 = t * BT;
         bool masked = key0 + BT > a.Sk;
         if (a.causal) masked = masked || (t >= nf && w_qmin < pos_of(kvp, min(key0 + BT, a.Sk) - 1));
-        int lim = BT + 64;  // no masking
-        if (masked) lim = (a.causal ? clamp32(count_le(kvp, my_qpos), 0, a.Sk) : a.Sk) - key0 - hh * 4;
         bf16x8 dsb[4];
+        if (masked) {  // a tile on the causal boundary or the ragged end: mask by prefix length
+          const int lim = (a.causal ? clamp32(count_le(kvp, my_qpos), 0, a.Sk) : a.Sk) - key0 - hh * 4;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+          for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int off = kb * 32 + (r >> 2) * 8 + (r & 3);
-            const float p = off < lim ? __builtin_amdgcn_exp2f(fmaf(sc[kb][r], sl2, -lse2)) : 0.f;
-            dsb[kb * 2 + (r >> 3)][r & 7] = (__bf16)(p * (dp[kb][r] - dlt));
-          }
+            for (int r = 0; r < 16; ++r) {
+              const int off = kb * 32 + (r >> 2) * 8 + (r & 3);
+              const float p = off < lim ? __builtin_amdgcn_exp2f(fmaf(sc[kb][r], sl2, -lse2)) : 0.f;
+              dsb[kb * 2 + (r >> 3)][r & 7] = (__bf16)(p * (dp[kb][r] - dlt));
+            }
+        } else {
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const float p = __builtin_amdgcn_exp2f(fmaf(sc[kb][r], sl2, -lse2));
+              dsb[kb * 2 + (r >> 3)][r & 7] = (__bf16)(p * (dp[kb][r] - dlt));
+            }
+        }
         // dQ^T += K^T dS^T, 16 keys per MFMA
 #pragma unroll
         for (int ch = 0; ch < 4; ++ch)
@@ -355,7 +371,7 @@ __global__ __launch_bounds__(NT, RA_DKDV_WG_PER_CU) void dkdv_kernel(const BwdAr
       copy_tile<D>(rows_rsrc(qbase + (int64_t)q0 * rowb_q, rows, rowb_q), q_l, rowb_q, wave, lane);
       copy_tile<D>(rows_rsrc(obase + (int64_t)q0 * rowb_q, rows, rowb_q), o_l, rowb_q, wave, lane);
       if (wave < 2) {
-        const float* src = (wave == 0 ? a.lse : a.delta) + srow0 + q0;
+        const float* src = (wave == 0 ? a.lse2 : a.delta) + srow0 + q0;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rows_rsrc((const char*)src, rows, 4),
                                                  (__attribute__((address_space(3))) void*)(wave == 0 ? lse_l : dlt_l),
                                                  4, (uint32_t)lane * 4, 0, 0, 0);
@@ -386,7 +402,7 @@ __global__ __launch_bounds__(NT, RA_DKDV_WG_PER_CU) void dkdv_kernel(const BwdAr
               const int r = 4 * j + e;
               const int iq = q0 + qb * 32 + 8 * j + 4 * hh + e;  // local query index
               const bool vis = !masked || (iq < a.Sq && (!a.causal || iq >= qfirst));
-              const float p = vis ? __builtin_amdgcn_exp2f(fmaf(sc[r], sl2, -ls[e] * kLog2e)) : 0.f;
+              const float p = vis ? __builtin_amdgcn_exp2f(fmaf(sc[r], sl2, -ls[e])) : 0.f;
               pb[r >> 3][r & 7] = (__bf16)p;
               dsb[r >> 3][r & 7] = (__bf16)(p * (dp[r] - dl[e]));
             }
@@ -447,7 +463,8 @@ hipError_t launch_attn_bwd(const BwdArgs& a, int D, hipStream_t stream) {
   const int64_t rows = (int64_t)a.B * a.Sq * a.H;
   if (rows == 0) return hipSuccess;
   hipLaunchKernelGGL(delta_kernel, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, stream,
-                     (const __bf16*)a.o, (const __bf16*)a.dout, a.delta, (int64_t)a.B, (int64_t)a.Sq, (int64_t)a.H, D);
+                     (const __bf16*)a.o, (const __bf16*)a.dout, a.lse, a.delta, a.lse2, (int64_t)a.B, (int64_t)a.Sq,
+                     (int64_t)a.H, D);
   const int64_t gq = (int64_t)((a.Sq + QT - 1) / QT) * a.B * a.H;
   const int64_t gk = (int64_t)((a.Sk + KT - 1) / KT) * a.B * a.Hkv * a.nsteps;
   if (D == 128) {

@@ -352,7 +352,7 @@ int ra_debug_tile_counts(const void* q, const void* const* k_shares, const void*
 
 size_t ra_ring_share_bwd_workspace_bytes(int64_t B, int64_t H, int64_t S_loc) {
   if (B < 0 || H < 0 || S_loc < 0) return 0;
-  return (size_t)4 * (size_t)(B * H * S_loc);
+  return (size_t)8 * (size_t)(B * H * S_loc);
 }
 
 }  // extern "C"
@@ -393,7 +393,7 @@ int ring_share_bwd_impl(const void* q, const void* const* k_shares, const void* 
   }
   if (noalloc) {
     if (ra_ring_share_bwd_workspace_bytes(B, H, S_loc) > (size_t)RA_BWD_NOALLOC_MAX_BYTES)
-      return fail(RA_ERR_UNSUPPORTED, "B*H*S_loc = %lld row terms need %zu bytes, above the %d-byte device scratch",
+      return fail(RA_ERR_UNSUPPORTED, "B*H*S_loc = %lld rows' terms need %zu bytes, above the %d-byte device scratch",
                   (long long)(B * H * S_loc), ra_ring_share_bwd_workspace_bytes(B, H, S_loc),
                   RA_BWD_NOALLOC_MAX_BYTES);
     float* p = nullptr;
@@ -415,6 +415,7 @@ int ring_share_bwd_impl(const void* q, const void* const* k_shares, const void* 
   a.dout = dout;
   a.lse = lse;
   a.delta = (float*)ws;
+  a.lse2 = a.delta + B * H * S_loc;
   a.dq = dq;
   for (int s = 0; s < N; ++s) {
     const int src = ((rank - s) % N + N) % N;  // ring order, as in the forward

@@ -103,6 +103,7 @@ struct BwdArgs {
   const void* dout;     // dO [B, Sq, H, D]
   const float* lse;     // forward LSE [B, H, Sq] (natural log)
   float* delta;         // workspace [B, H, Sq]: rowsum(dO * O)
+  float* lse2;          // workspace [B, H, Sq]: LSE * log2 e (+inf for a row with no visible key)
   float* dq;            // [B, Sq, H, D]
   const void* k[kMaxSteps];
   const void* v[kMaxSteps];

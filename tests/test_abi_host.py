@@ -140,7 +140,7 @@ def call_bwd(**over):
 
 
 def test_ring_share_bwd_validation():
-    assert lib.ra_ring_share_bwd_workspace_bytes(2, 3, 100) == 4 * 2 * 3 * 100
+    assert lib.ra_ring_share_bwd_workspace_bytes(2, 3, 100) == 8 * 2 * 3 * 100
     assert call_bwd(ind=0) == UNSUP                       # fp32 inputs: forward only
     assert call_bwd(D=96) == UNSUP
     assert call_bwd(N=0) == INVALID
@@ -148,7 +148,7 @@ def test_ring_share_bwd_validation():
     assert call_bwd(Hkv=3, H=4) == SHAPE
     assert call_bwd(assign=2, S=63) == SHAPE
     assert call_bwd(ws=None) == INVALID
-    assert call_bwd(wsb=4 * 2 * 64 - 4) == INVALID
+    assert call_bwd(wsb=8 * 2 * 64 - 4) == INVALID
     assert call_bwd(dq=ctypes.c_void_p(0x10004)) == MISALIGNED
     nulls = (ctypes.c_void_p * 4)(0x10000, 0x10000, 0, 0x10000)
     assert call_bwd(dvs=nulls) == INVALID
@@ -157,12 +157,12 @@ def test_ring_share_bwd_validation():
 
 def test_ring_share_bwd_noalloc_validation():
     # same checks as the workspace form, plus the size of the static device scratch (16 MiB of
-    # fp32 row terms), all on the host
+    # row terms, 8 bytes per (batch, head, row)), all on the host
     f = lib.ra_ring_share_bwd_noalloc
     arr = (ctypes.c_void_p * 2)(0x10000, 0x10000)
     args = lambda **o: [o.get(k, v) for k, v in (("q", FAKE), ("ks", arr), ("vs", arr), ("o", FAKE), ("lse", FAKE),
                                                  ("do", FAKE), ("dq", FAKE), ("dks", arr), ("dvs", arr), ("B", 1),
-                                                 ("H", 64), ("Hkv", 64), ("S", 65536), ("D", 128), ("N", 2), ("rank", 0),
+                                                 ("H", 32), ("Hkv", 32), ("S", 65536), ("D", 128), ("N", 2), ("rank", 0),
                                                  ("assign", 0), ("causal", 1), ("ind", 1), ("scale", 0.0), ("st", None))]
     assert f(*args(S=65536 + 64)) == UNSUP and "scratch" in _lib.last_error()
     assert f(*args(ind=0)) == UNSUP

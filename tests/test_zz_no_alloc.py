@@ -68,9 +68,9 @@ def test_noalloc_matches_workspace_form_twice():
 
 
 def test_noalloc_rejects_sizes_beyond_the_scratch():
-    # 4 * B * H * S_loc bytes of row terms must fit the 16 MiB array
+    # 8 * B * H * S_loc bytes of row terms must fit the 16 MiB array
     fake = ctypes.c_void_p(0x10000)
     arr = (ctypes.c_void_p * 2)(0x10000, 0x10000)
-    rc = lib.ra_ring_share_bwd_noalloc(fake, arr, arr, fake, fake, fake, fake, arr, arr, 1, 64, 64, 65536 + 64, 128,
+    rc = lib.ra_ring_share_bwd_noalloc(fake, arr, arr, fake, fake, fake, fake, arr, arr, 1, 32, 32, 65536 + 64, 128,
                                        2, 0, 0, 1, BF16, 0.0, None)
     assert rc == -2 and "scratch" in lib.ra_last_error().decode()
