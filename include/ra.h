@@ -36,6 +36,9 @@
  *     key tiles); "always" pairs every causal call with two or more query tiles (unless
  *     the key split applies), "never" keeps one tile per workgroup. Results agree to
  *     rounding either way; read at every launch.
+ *   - Environment: RA_PAIR_GROUP. Paired workgroups visit a step's key tiles in groups (tiles
+ *     of one step, then the same range of the next step): of 8 tiles for K/V shares of at most
+ *     8192 rows, of 32 otherwise; "short" / "long" force 8 / 32. Results agree to rounding.
  */
 #ifndef RA_H_
 #define RA_H_

@@ -100,11 +100,22 @@ constexpr float kLn2 = 0.6931471805599453f;
 #ifndef RA_ATTN_DMA_REGS
 #define RA_ATTN_DMA_REGS 0            // keep the lanes' copy offsets in registers for the whole loop
 #endif
+#ifndef RA_ATTN_TILE_GROUP_PAIR
+#define RA_ATTN_TILE_GROUP_PAIR RA_ATTN_TILE_GROUP  // the same for paired query tiles of long shares
+#endif
+#ifndef RA_ATTN_TILE_GROUP_SHORT
+#define RA_ATTN_TILE_GROUP_SHORT 8    // paired query tiles of short shares (PAIR = 2)
+#endif
+#ifndef RA_ATTN_SHORT_SHARE
+#define RA_ATTN_SHORT_SHARE 8192      // K/V shares of at most this many rows count as short
+#endif
 #ifndef RA_ATTN_WAVES_PER_SIMD
 #define RA_ATTN_WAVES_PER_SIMD 2      // occupancy target: 256 VGPRs per wave at 2, 512 at 1
 #endif
 
-constexpr int TG = RA_ATTN_TILE_GROUP;
+constexpr int TG_ONE = RA_ATTN_TILE_GROUP;
+constexpr int TG_PAIR = RA_ATTN_TILE_GROUP_PAIR;
+constexpr int TG_SHORT = RA_ATTN_TILE_GROUP_SHORT;
 
 // Word 3 of a raw buffer resource (untyped 32-bit data, no swizzle, no stride): reads past
 // num_records return zeros.
@@ -207,7 +218,7 @@ __device__ __forceinline__ void sched_chunk(std::integer_sequence<int, I...>) {
 // query rows, group g folding the tiles at odd (g = 1) or even (g = 0) places of the sequence
 // into its own (m, l, O); the groups' states are merged through LDS at the end, like two
 // blocks of the ring merged by the log-sum-exp update. Each SIMD then holds two waves.
-// PAIR = 1 (striped shares on large grids): a workgroup takes the query tiles n_qt-1-p and p.
+// PAIR = 1 or 2 (striped shares on large grids): a workgroup takes the query tiles n_qt-1-p and p.
 // Under a causal mask a query tile's work grows linearly with its index, so every pair has the
 // same total; the first tile walks its (step, tile) sequence forward and the second backward,
 // so the workgroups resident at once read the same key tiles at the same time and finish
@@ -228,6 +239,8 @@ __global__ __launch_bounds__(NT * KVS, QB == 1 ? RA_ATTN_WAVES_PER_SIMD : 1) voi
   __shared__ __attribute__((aligned(1024))) __bf16 v_lds0[C::ELEMS * KVS];
   __shared__ __attribute__((aligned(1024))) __bf16 v_lds1[C::ELEMS * KVS];
 
+  // tiles of one step visited before the next step
+  constexpr int TG = PAIR == 2 ? TG_SHORT : (PAIR ? TG_PAIR : TG_ONE);
   const int tid = threadIdx.x;
   const int wave_wg = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keep in SGPRs
   const int grp = KVS == 1 ? 0 : wave_wg / RA_ATTN_WAVES;        // key-split group
@@ -302,6 +315,16 @@ static int pair_override() {
   return 0;
 }
 
+// RA_PAIR_GROUP override of the paired kernels' tile-group size: 1 "long" (groups of 32 tiles),
+// -1 "short" (groups of 8), 0 automatic (short for K/V shares of at most RA_ATTN_SHORT_SHARE rows).
+static int pair_group_override() {
+  const char* e = getenv("RA_PAIR_GROUP");
+  if (!e) return 0;
+  if (!strcmp(e, "long")) return 1;
+  if (!strcmp(e, "short")) return -1;
+  return 0;
+}
+
 template <int KVS, int PAIR, int DBG>
 static void launch_dbg(const AttnArgs& a, int D, int o_dtype, dim3 g, hipStream_t stream) {
   dim3 blk(NT * KVS);
@@ -340,7 +363,11 @@ hipError_t launch_attn_bf16(const AttnArgs& a, int D, int o_dtype, hipStream_t s
   const bool pair = a.causal && n_qt >= 2 &&
                     (pmode > 0 || (pmode == 0 && a.kv_assign == RA_STRIPED && pairs >= 2 * (int64_t)device_cus()));
   if (pair) {
-    launch<1, 1>(a, D, o_dtype, dim3((unsigned)pairs), stream);
+    // Short shares (a few dozen key tiles per step) keep the paired workgroups of a head on the
+    // same key tiles better with groups of 8 tiles; long shares with groups of 32.
+    const int gmode = pair_group_override();
+    if (gmode < 0 || (gmode == 0 && a.Sk <= RA_ATTN_SHORT_SHARE)) launch<1, 2>(a, D, o_dtype, dim3((unsigned)pairs), stream);
+    else launch<1, 1>(a, D, o_dtype, dim3((unsigned)pairs), stream);
     return hipGetLastError();
   }
   launch<1, 0>(a, D, o_dtype, dim3((unsigned)grid), stream);

@@ -6,7 +6,8 @@ grids large enough to fill the GPU twice over, which the small parity cases neve
 tests rerun them with pairing forced, so ragged tails, odd tile counts (a middle tile left
 alone), resumed rings, tile-group boundaries, 64-step rings and grouped KV heads all go through
 the paired path (the unsplit layout: RA_KV_SPLIT=never, since pairing is not combined with the
-key split). The oracle comparisons are those of test_gpu_kernels.
+key split), with the tile groups of 8 and of 32 tiles (RA_PAIR_GROUP). The oracle comparisons are
+those of test_gpu_kernels.
 """
 import pytest
 import torch
@@ -25,10 +26,12 @@ def _gpu():
     torch.cuda.set_device(0)
 
 
-@pytest.fixture(autouse=True)
-def _always_pair(monkeypatch):
+@pytest.fixture(autouse=True, params=["short", "long"])
+def _always_pair(monkeypatch, request):
+    # both paired instantiations: tile groups of 8 (chosen for short shares) and of 32
     monkeypatch.setenv("RA_PAIR_TILES", "always")
     monkeypatch.setenv("RA_KV_SPLIT", "never")
+    monkeypatch.setenv("RA_PAIR_GROUP", request.param)
 
 
 @pytest.mark.parametrize("case", K.RING_CASES, ids=[f"{a}-N{n}-L{l}" for a, n, l in K.RING_CASES])

@@ -71,7 +71,8 @@ def run_case(assign, n, s_loc, h, d, causal, b=1, seed=2100):
 
 
 @pytest.mark.parametrize("layout", [{}, {"RA_KV_SPLIT": "always"}, {"RA_KV_SPLIT": "never"},
-                                    {"RA_PAIR_TILES": "always", "RA_KV_SPLIT": "never"}])
+                                    {"RA_PAIR_TILES": "always", "RA_KV_SPLIT": "never"},
+                                    {"RA_PAIR_TILES": "always", "RA_KV_SPLIT": "never", "RA_PAIR_GROUP": "long"}])
 @pytest.mark.parametrize("assign", ["contiguous", "striped", "zigzag"])
 @pytest.mark.parametrize("n,s_loc,causal", [(4, 256, True), (3, 200, True), (8, 384, True), (1, 520, True),
                                             (4, 200, False)])
