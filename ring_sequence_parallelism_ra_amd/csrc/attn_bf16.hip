@@ -91,9 +91,6 @@ constexpr float kLn2 = 0.6931471805599453f;
 #ifndef RA_ATTN_MUL24
 #define RA_ATTN_MUL24 1               // 24-bit multiply for the copies' row offsets (rows < 2^24 bytes)
 #endif
-#ifndef RA_ATTN_MAX_TREE
-#define RA_ATTN_MAX_TREE 0            // tile maxima as a tree (short dependency chain)
-#endif
 #ifndef RA_ATTN_SOFFSET
 #define RA_ATTN_SOFFSET 1             // the copies' wave-uniform row offset as the scalar offset
 #endif
@@ -158,29 +155,6 @@ struct OutF32 {
 __device__ inline float pair_max(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-// Maximum of the 16*NB scores a lane holds, as a tree of three-input maxima (depth 4 for 32
-// scores instead of a chain of 16 dependent operations).
-template <int NB>
-__device__ inline float tree_max(const f32x16 (&s)[NB]) {
-  constexpr int N = 16 * NB;
-  float v[N];
-#pragma unroll
-  for (int i = 0; i < N; ++i) v[i] = s[i / 16][i % 16];
-  int n = N;
-#pragma unroll
-  for (int level = 0; level < 6; ++level) {
-    if (n == 1) break;
-    int m = 0;
-#pragma unroll
-    for (int i = 0; i < n; i += 3) {
-      if (i + 2 < n) v[m++] = fmaxf(fmaxf(v[i], v[i + 1]), v[i + 2]);
-      else if (i + 1 < n) v[m++] = fmaxf(v[i], v[i + 1]);
-      else v[m++] = v[i];
-    }
-    n = m;
-  }
-  return v[0];
 }
 __device__ inline float pair_sum(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
