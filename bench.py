@@ -129,7 +129,26 @@ def time_calls(fn, steps, warmup, settle_s=0.0):
     return wall, sum(ev) / len(ev), sorted(ev)[len(ev) // 2]
 
 
-def bench_ring(name, steps, warmup, settle_s=0.0):
+def tile_walk(inp, w):
+    """Tiles the kernel really visits on a ring workload, counted on the device by the
+    tile-counting copy of the kernel (one untimed call), next to the planner's tile classes:
+    the skipped upper triangle of the causal matrix."""
+    import ring_sequence_parallelism_ra_amd as ra
+    _, _, cnt = ra.debug_tile_counts(inp["q"], inp["k"], inp["v"], w.rank, assign=w.assign)
+    c = cnt.cpu().long()
+    folded = int(c[..., 0].sum()) // 4           # each of the 4 waves of a query tile folds every tile
+    masked = int(c[..., 1].sum())
+    n, L, s = w.world, w.global_len, w.share_len
+    bm, bn = ra.tile_shape(ra.BF16, w.head_dim)
+    q_sh = ra.Shard(w.assign, n, w.rank, L)
+    cls = [ra.share_work(q_sh, ra.Shard(w.assign, n, src, L), s, s, True, bm, bn) for src in range(n)]
+    full, part, skip = (sum(x[i] for x in cls) * w.batch * w.heads for i in (1, 2, 3))
+    return {"visited_tiles": folded, "planner_full_plus_partial": full + part, "skipped_tiles": skip,
+            "skipped_fraction": round(skip / (full + part + skip), 4), "masked_wave_tiles": masked,
+            "masked_fraction_of_wave_tiles": round(masked / max(1, 4 * folded), 5)}
+
+
+def bench_ring(name, steps, warmup, settle_s=0.0, tiles=False):
     import torch
 
     import ring_sequence_parallelism_ra_amd as ra
@@ -143,6 +162,8 @@ def bench_ring(name, steps, warmup, settle_s=0.0):
     wall, ev_mean, ev_med = time_calls(call, steps, warmup, settle_s)
     res = {"tflops": flops / (wall * 1e-3) / 1e12, "kernel_ms_mean": ev_mean, "kernel_ms_median": ev_med,
            "kernel_ms_min": TIMES[id(call)]["min"], "ms_per_step": wall, "flops": flops}
+    if tiles:
+        res["tile_walk"] = tile_walk(inp, w)
     del inp, o, lse
     torch.cuda.empty_cache()
     return res, host, w
@@ -534,14 +555,14 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
 
-    head, host, w = bench_ring(HEADLINE, args.steps, args.warmup)
+    head, host, w = bench_ring(HEADLINE, args.steps, args.warmup, tiles=True)
     log(f"[bench] {HEADLINE}: {head['tflops']:.1f} TFLOP/s, kernel {head['kernel_ms_mean']:.3f} ms")
     achieved = head["flops"] / (head["kernel_ms_mean"] * 1e-3) / 1e12
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic_for(head["kernel_ms_mean"]),
                 "kernel": "attn_bf16_kernel<128, OutBf16, 1, 0, 0>", "kernel_ms": round(head["kernel_ms_mean"], 4),
                 "kernel_ms_min": round(head["kernel_ms_min"], 4), "kernel_ms_median": round(head["kernel_ms_median"], 4),
-                "flops_per_launch": head["flops"]}
+                "flops_per_launch": head["flops"], "tile_walk": head["tile_walk"]}
 
     secondary = {}
     if chosen:

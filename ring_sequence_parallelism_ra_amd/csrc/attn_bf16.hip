@@ -91,6 +91,9 @@ constexpr float kLn2 = 0.6931471805599453f;
 #ifndef RA_ATTN_MUL24
 #define RA_ATTN_MUL24 1               // 24-bit multiply for the copies' row offsets (rows < 2^24 bytes)
 #endif
+#ifndef RA_ATTN_SCHED_FIRST
+#define RA_ATTN_SCHED_FIRST 44        // VALU ops placed before the first MFMA of the main block
+#endif
 #ifndef RA_ATTN_SOFFSET
 #define RA_ATTN_SOFFSET 1             // the copies' wave-uniform row offset as the scalar offset
 #endif
