@@ -138,6 +138,7 @@ def tile_walk(inp, w):
     c = cnt.cpu().long()
     folded = int(c[..., 0].sum()) // 4           # each of the 4 waves of a query tile folds every tile
     masked = int(c[..., 1].sum())
+    faults = int(c[..., 2].sum()) + int(c[..., 3].sum())
     n, L, s = w.world, w.global_len, w.share_len
     bm, bn = ra.tile_shape(ra.BF16, w.head_dim)
     q_sh = ra.Shard(w.assign, n, w.rank, L)
@@ -145,7 +146,7 @@ def tile_walk(inp, w):
     full, part, skip = (sum(x[i] for x in cls) * w.batch * w.heads for i in (1, 2, 3))
     return {"visited_tiles": folded, "planner_full_plus_partial": full + part, "skipped_tiles": skip,
             "skipped_fraction": round(skip / (full + part + skip), 4), "masked_wave_tiles": masked,
-            "masked_fraction_of_wave_tiles": round(masked / max(1, 4 * folded), 5)}
+            "masked_fraction_of_wave_tiles": round(masked / max(1, 4 * folded), 5), "walk_faults": faults}
 
 
 def bench_ring(name, steps, warmup, settle_s=0.0, tiles=False):

@@ -279,7 +279,7 @@ int ra_debug_mask(const ra_shard* q_sh, const ra_shard* kv_sh, int64_t Sq, int64
  * §3.4): these calls show which K/V tiles the bf16 kernel actually visits.
  *
  * ra_debug_tile_count_slots: int32 slots ra_debug_tile_counts writes for a share of S_loc query
- * rows: ceil(S_loc / block_m) * B * H * 16 (block_m from ra_tile_shape, 128 for bf16).
+ * rows: ceil(S_loc / block_m) * B * H * 32 (block_m from ra_tile_shape, 128 for bf16).
  *
  * ra_debug_tile_counts: the same computation and outputs as ra_ring_share over every ring step
  * (start_step 0, num_steps N, no workspace) with bf16 inputs, run through a copy of the bf16
@@ -287,8 +287,13 @@ int ra_debug_mask(const ra_shard* q_sh, const ra_shard* kv_sh, int64_t Sq, int64
  * 32 query rows and, among those, the tiles on which it evaluates the mask (a tile is masked by
  * a wave when it is the ragged last tile of a share or when the wave's first query row does not
  * see the tile's last key). The workgroup layout (one query tile, key split, paired tiles) is
- * chosen exactly as for ra_ring_share. Output counts, int32 [ceil(S_loc/128), B, H, 8, 2]:
- * [qt, b, h, w, 0] = tiles folded in by wave slot w of query tile qt, [.., 1] = tiles it masked.
+ * chosen exactly as for ra_ring_share. Output counts, int32 [ceil(S_loc/128), B, H, 8, 4]:
+ * [qt, b, h, w, 0] = tiles folded in by wave slot w of query tile qt, [.., 1] = tiles it masked,
+ * [.., 2] = bounds faults: tiles the wave copied or folded whose (step, tile) cursor lies outside
+ * the call's steps or past the step's last visible tile or the share's end, [.., 3] = skip
+ * faults: tiles it folded whose first key no query row of the query tile sees (causal). The
+ * two fault counts are zero for a correct kernel; they are checked, not asserted, so a fault
+ * is reported through the counts and never stops the kernel.
  * Wave slots 0-3 are the four waves of the first (or only) wave group, 4-7 those of the second
  * group of a key-split workgroup (zero otherwise); a wave whose rows all lie past S_loc counts
  * nothing. counts is a device buffer of counts_len >= ra_debug_tile_count_slots(..) slots,

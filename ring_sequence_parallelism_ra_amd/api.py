@@ -319,8 +319,8 @@ def debug_mask(q_shard, kv_shard, Sq, Sk, device="cuda", stream=None):
 def debug_tile_counts(q, k_shares, v_shares, rank, *, assign="contiguous", causal=True, scale=0.0,
                       out_dtype=None, stream=None):
     """ring_share through the tile-counting copy of the bf16 kernel; returns (O, LSE, counts) with
-    counts int32 [ceil(S_loc/128), B, H, 8, 2] (per wave slot: tiles folded in, tiles masked);
-    see ra_debug_tile_counts."""
+    counts int32 [ceil(S_loc/128), B, H, 8, 4] (per wave slot: tiles folded in, tiles masked,
+    bounds faults, skip faults); see ra_debug_tile_counts."""
     b, s, h, d = q.shape
     _expect(q, "q", q.shape, torch.bfloat16)
     n = len(k_shares)
@@ -341,7 +341,7 @@ def debug_tile_counts(q, k_shares, v_shares, rank, *, assign="contiguous", causa
     check(lib.ra_debug_tile_counts(_p(q), kp, vp, _p(o), _p(lse), b, h, hkv, s, d, n, rank, ASSIGN.get(assign, assign),
                                    1 if causal else 0, _dt(o), float(scale), _p(counts), counts.numel(),
                                    _stream(stream)))
-    return o, lse, counts[:slots].view(-1, b, h, 8, 2)
+    return o, lse, counts[:slots].view(-1, b, h, 8, 4)
 
 
 def torch_dtype(code: int):

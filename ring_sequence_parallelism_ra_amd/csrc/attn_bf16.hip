@@ -202,7 +202,9 @@ __device__ __forceinline__ void sched_chunk(std::integer_sequence<int, I...>) {
 // together (unpaired, the striped share's late-starting workgroups walk out of step with the
 // running ones and miss in L2).
 // DBG = 1 (debug hook only, never a product launch): every wave also counts the K/V tiles it
-// folds in and those on which it evaluates the mask, and writes both to a.dbg_counts.
+// folds in, those on which it evaluates the mask, and two kinds of fault that a correct walk
+// never shows (a copied or folded tile outside its step's visible tiles, a folded tile that no
+// query row of the tile sees), and writes the four counts to a.dbg_counts.
 template <int D, class Out, int KVS, int PAIR, int DBG>
 __global__ __launch_bounds__(NT * KVS, QB == 1 ? RA_ATTN_WAVES_PER_SIMD : 1) void attn_bf16_kernel(const AttnArgs a) {
   using C = Cfg<D>;

@@ -331,7 +331,7 @@ int ra_ring_share(const void* q, const void* const* k_shares, const void* const*
 
 int64_t ra_debug_tile_count_slots(int64_t B, int64_t H, int64_t S_loc) {
   if (B < 0 || H < 0 || S_loc < 0) return 0;
-  return (S_loc + ra::kBf16BlockM - 1) / ra::kBf16BlockM * B * H * 16;
+  return (S_loc + ra::kBf16BlockM - 1) / ra::kBf16BlockM * B * H * 32;
 }
 
 int ra_debug_tile_counts(const void* q, const void* const* k_shares, const void* const* v_shares, void* o,

@@ -121,7 +121,7 @@ static void validation() {
         RA_ERR_INVALID_ARG);
 
   // debug hooks
-  CHECK(ra_debug_tile_count_slots(2, 3, 300) == 3 * 2 * 3 * 16);
+  CHECK(ra_debug_tile_count_slots(2, 3, 300) == 3 * 2 * 3 * 32);
   CHECK(ra_debug_tile_counts(FAKE, shares.data(), shares.data(), FAKE, (float*)FAKE, 1, 2, 2, 64, 128, 4, 0,
                              RA_STRIPED, 1, RA_BF16, 0.f, (int32_t*)FAKE, 1, 0) == RA_ERR_INVALID_ARG);
   ra_shard p = {RA_ZIGZAG, 8, 3, 262144};

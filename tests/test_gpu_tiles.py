@@ -2,7 +2,8 @@
 tiles each wave actually folds in (every tile with a visible pair for its query tile, none of
 the skipped upper triangle of the causal matrix, [Digest] §3.4) and the tiles on which it
 evaluates the mask, exactly, in every workgroup layout, with the counting copy's outputs
-bit-identical to the product call's."""
+bit-identical to the product call's; the counting copy's own per-tile bounds and visibility
+checks report no fault."""
 import numpy as np
 import pytest
 import torch
@@ -32,9 +33,13 @@ def expected(assign, n, r, L, causal):
 
 
 def check_counts(counts, vis, msk, s_loc, what):
-    c = counts.cpu().numpy().astype(np.int64)           # [n_qt, B, H, 8, 2]
+    c = counts.cpu().numpy().astype(np.int64)           # [n_qt, B, H, 8, 4]
     n_qt = c.shape[0]
     assert vis.shape == (n_qt,), what
+    # the walk's own checks: no copied or folded tile outside its step's visible tiles, no
+    # folded tile that the query tile cannot see
+    assert not c[..., 2].any(), f"{what}: bounds faults {int(c[..., 2].sum())}"
+    assert not c[..., 3].any(), f"{what}: folded tiles no query row sees {int(c[..., 3].sum())}"
     fold = c[..., 0]
     mask = c[..., 1]
     # the two wave groups of a key-split workgroup share the query rows: sum them per wave
