@@ -392,6 +392,16 @@ __global__ __launch_bounds__(NT, RA_DKDV_WG_PER_CU) void dkdv_kernel(const BwdAr
                                                          read_r<D>(v_l, of, ks, wave * 32), dp, 0, 0, 0);
           }
           // register r of lane l holds query qb*32 + 8*(r/4) + 4*(l/32) + r%4 and key l%32
+          if (masked) {
+            // scores of pairs the key does not see (or of rows past the share) become -inf, so
+            // their weights below come out 0 with no branch per score (a guarded exp2 compiles
+            // to a branch on the lane mask for every score)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int iq = q0 + qb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);  // local query index
+              sc[r] = ((iq < a.Sq) & (!a.causal | (iq >= qfirst))) ? sc[r] : -INFINITY;
+            }
+          }
           bf16x8 pb[2], dsb[2];
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
@@ -400,9 +410,8 @@ __global__ __launch_bounds__(NT, RA_DKDV_WG_PER_CU) void dkdv_kernel(const BwdAr
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               const int r = 4 * j + e;
-              const int iq = q0 + qb * 32 + 8 * j + 4 * hh + e;  // local query index
-              const bool vis = !masked || (iq < a.Sq && (!a.causal || iq >= qfirst));
-              const float p = vis ? __builtin_amdgcn_exp2f(fmaf(sc[r], sl2, -ls[e])) : 0.f;
+              // LSE is finite, or +inf for a row with no visible key: the weight is 0 there too
+              const float p = __builtin_amdgcn_exp2f(fmaf(sc[r], sl2, -ls[e]));
               pb[r >> 3][r & 7] = (__bf16)p;
               dsb[r >> 3][r & 7] = (__bf16)(p * (dp[r] - dl[e]));
             }
