@@ -38,8 +38,8 @@ def striped(world: int, rank: int, global_len: int) -> np.ndarray:
     """Striped split: token t goes to rank t mod N ([Digest] §4, striped listing:
     GPU0 holds 0, 4, 8, 12 of 16 tokens on 4 GPUs)."""
     _check(world, rank, global_len, world)
-    t = np.arange(global_len, dtype=np.int64)
-    return t[t % world == rank]
+    # the tokens t with t mod N == r, in ascending order: r, r + N, r + 2N, ...
+    return np.arange(rank, global_len, world, dtype=np.int64)
 
 
 def zigzag(world: int, rank: int, global_len: int) -> np.ndarray:
