@@ -52,6 +52,12 @@ constexpr int QT = 128;      // dq_kernel: query rows per workgroup (32 per wave
 constexpr int KT = 128;      // dkdv_kernel: keys per workgroup (32 per wave)
 constexpr int BT = 64;       // rows of a streamed tile (keys in dq_kernel, queries in dkdv_kernel)
 static_assert(KT % BT == 0, "the dK/dV kernel stages its V rows as whole tiles");
+#ifndef RA_DQ_SCHED
+#define RA_DQ_SCHED 1        // dQ kernel: interleave each chunk's dQ MFMAs with the next chunk's dS work
+#endif
+#ifndef RA_DQ_SCHED_FIRST
+#define RA_DQ_SCHED_FIRST 36  // vector ops of the first chunk ahead of the first dQ MFMA
+#endif
 #ifndef RA_DKDV_WG_PER_CU
 #define RA_DKDV_WG_PER_CU 2  // dK/dV workgroups resident per CU (registers per lane: 512 / this)
 #endif
@@ -252,32 +258,44 @@ __global__ __launch_bounds__(NT, 2) void dq_kernel(const BwdArgs a) {
         const int key0 = t * BT;
         bool masked = key0 + BT > a.Sk;
         if (a.causal) masked = masked || (t >= nf && w_qmin < pos_of(kvp, min(key0 + BT, a.Sk) - 1));
-        bf16x8 dsb[4];
-        if (masked) {  // a tile on the causal boundary or the ragged end: mask by prefix length
+        if (masked) {
+          // a tile on the causal boundary or the ragged end: the scores of keys past the row's
+          // visible prefix become -inf (weight 0), so the weights below need no mask and no
+          // branch per score
           const int lim = (a.causal ? clamp32(count_le(kvp, my_qpos), 0, a.Sk) : a.Sk) - key0 - hh * 4;
 #pragma unroll
           for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
               const int off = kb * 32 + (r >> 2) * 8 + (r & 3);
-              const float p = off < lim ? __builtin_amdgcn_exp2f(fmaf(sc[kb][r], sl2, -lse2)) : 0.f;
-              dsb[kb * 2 + (r >> 3)][r & 7] = (__bf16)(p * (dp[kb][r] - dlt));
-            }
-        } else {
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const float p = __builtin_amdgcn_exp2f(fmaf(sc[kb][r], sl2, -lse2));
-              dsb[kb * 2 + (r >> 3)][r & 7] = (__bf16)(p * (dp[kb][r] - dlt));
+              sc[kb][r] = off < lim ? sc[kb][r] : -INFINITY;
             }
         }
-        // dQ^T += K^T dS^T, 16 keys per MFMA
+        // dS of each 16-key chunk, then dQ^T += K^T dS^T for its keys (one MFMA per 32 head-dim
+        // rows); the MFMAs of a chunk issue between the vector work of the next one
+        bf16x8 dsb[4];
 #pragma unroll
-        for (int ch = 0; ch < 4; ++ch)
+        for (int ch = 0; ch < 4; ++ch) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int kb = ch >> 1, r = (ch & 1) * 8 + e;
+            const float p = __builtin_amdgcn_exp2f(fmaf(sc[kb][r], sl2, -lse2));
+            dsb[ch][e] = (__bf16)(p * (dp[kb][r] - dlt));
+          }
 #pragma unroll
           for (int db = 0; db < D / 32; ++db)
             dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_t<D>(kt, of, db, ch * 16), dsb[ch], dq[db], 0, 0, 0);
+        }
+#if RA_DQ_SCHED
+        __builtin_amdgcn_sched_group_barrier(0x002, RA_DQ_SCHED_FIRST, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+        for (int i = 0; i < 4 * (D / 32); ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, RA_DQ_SCHED_FIRST / (D / 32), 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+#endif
       }
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
