@@ -381,7 +381,9 @@ __global__ __launch_bounds__(NT, RA_DKDV_WG_PER_CU) void dkdv_kernel(const BwdAr
     const char* qbase = (const char*)a.q + ((int64_t)b * a.Sq * rs + (int64_t)h * D) * 2;
     const char* obase = (const char*)a.dout + ((int64_t)b * a.Sq * rs + (int64_t)h * D) * 2;
     const int64_t srow0 = ((int64_t)b * a.H + h) * a.Sq;
-    for (int qt = qt0; qt < n_qt; ++qt) {
+    // Query tiles from the last one down: every key tile's walk ends at the last query tile, so
+    // workgroups of a head that start together read the same Q and dO tiles together.
+    for (int qt = n_qt - 1; qt >= qt0; --qt) {
       const int q0 = qt * BT;
       const int rows = min(BT, a.Sq - q0);
       // Q and dO rows by 16-byte LDS DMA over all waves; LSE (natural log) and Delta by 4-byte
