@@ -28,6 +28,7 @@
 // the row so that 128-bit row reads stay conflict-free.
 #include <math.h>
 
+#include <algorithm>
 #include <mutex>
 
 #include "ra_internal.h"
@@ -148,25 +149,36 @@ __device__ inline bf16x8 read_r(const __bf16* tile, const Offsets<D>& of, int ks
 
 // Also stores the LSE in log2 units (lse2 = LSE * log2 e; +inf for a row with no visible key,
 // so that its weights come out 0), the form the dK/dV kernel takes its weights against.
+// D/8 consecutive lanes share one (b, s, h) row, 16 bytes of O and of dO each, so every load
+// instruction of a wave reads whole consecutive rows; the row's partial sums meet by shuffles.
+template <int D>
 __global__ __launch_bounds__(256) void delta_kernel(const __bf16* __restrict__ o, const __bf16* __restrict__ dout,
                                                     const float* __restrict__ lse, float* __restrict__ delta,
-                                                    float* __restrict__ lse2, int64_t B, int64_t S, int64_t H,
-                                                    int D) {
-  const int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // (b, s, h) row
-  if (u >= B * S * H) return;
-  const int64_t h = u % H, s = (u / H) % S, b = u / (H * S);
-  const bf16x8* po = (const bf16x8*)(o + u * D);
-  const bf16x8* pd = (const bf16x8*)(dout + u * D);
-  float acc = 0.f;
-  for (int c = 0; c < D / 8; ++c) {
-    const bf16x8 x = po[c], y = pd[c];
+                                                    float* __restrict__ lse2, int64_t B, int64_t S, int64_t H) {
+  constexpr int LPR = D / 8;      // lanes per row
+  constexpr int RPB = 256 / LPR;  // rows per workgroup
+  const int64_t rows = B * S * H;
+  const int c = threadIdx.x % LPR;
+  // workgroup-uniform loop over row groups (every lane takes part in the shuffles)
+  for (int64_t base = (int64_t)blockIdx.x * RPB; base < rows; base += (int64_t)gridDim.x * RPB) {
+    const int64_t u = base + threadIdx.x / LPR;  // (b, s, h) row
+    float acc = 0.f;
+    if (u < rows) {
+      const bf16x8 x = ((const bf16x8*)(o + u * D))[c];
+      const bf16x8 y = ((const bf16x8*)(dout + u * D))[c];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc = fmaf((float)x[e], (float)y[e], acc);
+      for (int e = 0; e < 8; ++e) acc = fmaf((float)x[e], (float)y[e], acc);
+    }
+#pragma unroll
+    for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, LPR);
+    if (u < rows && c == 0) {
+      const int64_t h = u % H, s = (u / H) % S, b = u / (H * S);
+      const int64_t r = (b * H + h) * S + s;
+      delta[r] = acc;
+      const float ln = lse[r];
+      lse2[r] = ln == -INFINITY ? INFINITY : ln * kLog2e;
+    }
   }
-  const int64_t r = (b * H + h) * S + s;
-  delta[r] = acc;
-  const float ln = lse[r];
-  lse2[r] = ln == -INFINITY ? INFINITY : ln * kLog2e;
 }
 
 template <int D>
@@ -491,9 +503,16 @@ hipError_t bwd_scratch(float** out) {
 hipError_t launch_attn_bwd(const BwdArgs& a, int D, hipStream_t stream) {
   const int64_t rows = (int64_t)a.B * a.Sq * a.H;
   if (rows == 0) return hipSuccess;
-  hipLaunchKernelGGL(delta_kernel, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, stream,
-                     (const __bf16*)a.o, (const __bf16*)a.dout, a.lse, a.delta, a.lse2, (int64_t)a.B, (int64_t)a.Sq,
-                     (int64_t)a.H, D);
+  const int64_t rpb = 256 / (D / 8);  // rows per delta_kernel workgroup and pass
+  const unsigned g_delta = (unsigned)std::min<int64_t>((rows + rpb - 1) / rpb, (int64_t)1 << 20);
+  if (D == 128)
+    hipLaunchKernelGGL(delta_kernel<128>, dim3(g_delta), dim3(256), 0, stream,
+                       (const __bf16*)a.o, (const __bf16*)a.dout, a.lse, a.delta, a.lse2, (int64_t)a.B, (int64_t)a.Sq,
+                       (int64_t)a.H);
+  else
+    hipLaunchKernelGGL(delta_kernel<64>, dim3(g_delta), dim3(256), 0, stream,
+                       (const __bf16*)a.o, (const __bf16*)a.dout, a.lse, a.delta, a.lse2, (int64_t)a.B, (int64_t)a.Sq,
+                       (int64_t)a.H);
   const int64_t gq = (int64_t)((a.Sq + QT - 1) / QT) * a.B * a.H;
   const int64_t gk = (int64_t)((a.Sk + KT - 1) / KT) * a.B * a.Hkv * a.nsteps;
   if (D == 128) {
