@@ -32,11 +32,33 @@ import collections
 import csv
 import hashlib
 import json
+import re
 import statistics
 
 
+def _demangle(name: str) -> str:
+    """The tracer leaves some template instances mangled (those with a __bf16 parameter): turn
+    ``_ZN<len><id>...<len><name>I<args>E...`` into ``name<args>`` for integer arguments."""
+    if not name.startswith("_ZN"):
+        return name
+    i, ident = 3, ""
+    while i < len(name) and name[i].isdigit():
+        j = i
+        while name[j].isdigit():
+            j += 1
+        n = int(name[i:j])
+        ident, i = name[j:j + n], j + n
+    args = []
+    if name[i:i + 1] == "I":
+        for m in re.finditer(r"Li(\d+)E", name[i + 1:]):
+            args.append(m.group(1))
+            if name[i + 1 + m.end():i + 2 + m.end()] == "E":
+                break
+    return ident + (f"<{', '.join(args)}>" if args else "") if ident else name
+
+
 def _short(name: str) -> str:
-    name = name.replace("ra::(anonymous namespace)::", "")
+    name = _demangle(name).replace("ra::(anonymous namespace)::", "")
     return name.split("(")[0].replace("void ", "").strip()
 
 

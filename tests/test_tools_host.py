@@ -120,3 +120,13 @@ def test_traffic_json_from_counters(tmp_path):
     assert t["write_bytes"] == round(20.0 * 1024)
     assert t["bytes_per_launch"] == t["fetch_bytes"] + t["write_bytes"]
     assert len(t["kernel_sha256_16"]) == 16
+
+
+def test_short_names_of_mangled_template_kernels():
+    # the tracer leaves kernels with a __bf16 parameter mangled; the summaries show them by name
+    sys.path.insert(0, ROOT)
+    import profile_summary as ps
+    assert ps._short("_ZN2ra12_GLOBAL__N_112delta_kernelILi128EEEvPKDF16bS3_PKfPfS6_lll") == "delta_kernel<128>"
+    assert ps._short("_ZN2ra12_GLOBAL__N_112delta_kernelILi64EEEvPKDF16bS3_PKfPfS6_lll") == "delta_kernel<64>"
+    assert ps._short("void ra::(anonymous namespace)::dq_kernel<128>(ra::BwdArgs)") == "dq_kernel<128>"
+    assert ps._short("__amd_rocclr_copyBuffer") == "__amd_rocclr_copyBuffer"
