@@ -57,6 +57,13 @@ def _demangle(name: str) -> str:
     return ident + (f"<{', '.join(args)}>" if args else "") if ident else name
 
 
+def _grid(r) -> int:
+    """Threads of a dispatch: a kernel trace gives the grid per dimension, a counter run the total."""
+    if "Grid_Size_X" in r:
+        return int(r["Grid_Size_X"]) * int(r.get("Grid_Size_Y") or 1) * int(r.get("Grid_Size_Z") or 1)
+    return int(r["Grid_Size"])
+
+
 def _short(name: str) -> str:
     name = _demangle(name).replace("ra::(anonymous namespace)::", "")
     return name.split("(")[0].replace("void ", "").strip()
@@ -73,7 +80,7 @@ def trace(args):
     run_no = collections.Counter()
     prev = None
     for r in rows:
-        key = (_short(r["Kernel_Name"]), int(r["Grid_Size_X"]))
+        key = (_short(r["Kernel_Name"]), _grid(r))
         label = ""
         if key in splits:
             if key != prev:
@@ -207,7 +214,7 @@ def pmc(args):
 def hbm(args):
     trace_rows = list(csv.DictReader(open(args.trace)))
     splits = _splits(args.split)
-    tgroups = _labelled(trace_rows, splits, lambda r: (_short(r["Kernel_Name"]), int(r["Grid_Size_X"])))
+    tgroups = _labelled(trace_rows, splits, lambda r: (_short(r["Kernel_Name"]), _grid(r)))
 
     def counter_groups(path, name):
         rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == name]

@@ -130,3 +130,13 @@ def test_short_names_of_mangled_template_kernels():
     assert ps._short("_ZN2ra12_GLOBAL__N_112delta_kernelILi64EEEvPKDF16bS3_PKfPfS6_lll") == "delta_kernel<64>"
     assert ps._short("void ra::(anonymous namespace)::dq_kernel<128>(ra::BwdArgs)") == "dq_kernel<128>"
     assert ps._short("__amd_rocclr_copyBuffer") == "__amd_rocclr_copyBuffer"
+
+
+def test_grid_of_a_dispatch_counts_every_dimension():
+    # a multi-tensor launch puts the tensor in blockIdx.y: its trace row must not share a grid
+    # key with the one-tensor launch of the same x extent
+    sys.path.insert(0, ROOT)
+    import profile_summary as ps
+    assert ps._grid({"Grid_Size_X": "4194304", "Grid_Size_Y": "3", "Grid_Size_Z": "1"}) == 12582912
+    assert ps._grid({"Grid_Size_X": "4194304"}) == 4194304
+    assert ps._grid({"Grid_Size": "12582912"}) == 12582912
