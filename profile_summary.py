@@ -94,6 +94,16 @@ def trace(args):
              "|---|---|---|---|---|---|---|"]
     for (k, g, lab), v in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
         lines.append(f"| {k} | {g} | {lab} | {len(v)} | {statistics.mean(v):.4f} | {min(v):.4f} | {max(v):.4f} |")
+        # --last KERNEL@GRID=LABEL:N adds a row for the last N calls of that group (the timed
+        # calls of a benchmark whose warm-up calls come first)
+        for spec in args.last:
+            key, rest = spec.split("=", 1)
+            kern, grid = key.rsplit("@", 1)
+            label, n = rest.rsplit(":", 1)
+            if k == kern and g == int(grid) and lab == label:
+                t = v[-int(n):]
+                lines.append(f"| {k} | {g} | {lab}, last {len(t)} calls | {len(t)} | {statistics.mean(t):.4f} "
+                             f"| {min(t):.4f} | {max(t):.4f} |")
     text = "\n".join(lines) + "\n"
     if args.note:
         text += "\n" + args.note + "\n"
@@ -282,6 +292,7 @@ def main():
     t.add_argument("--cmd", required=True)
     t.add_argument("--note", default="")
     t.add_argument("--split", action="append", default=[])
+    t.add_argument("--last", action="append", default=[], help="KERNEL@GRID=LABEL:N")
     w = sub.add_parser("traffic")
     w.add_argument("--fetch", required=True)
     w.add_argument("--write", required=True)

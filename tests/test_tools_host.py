@@ -68,6 +68,25 @@ def test_trace_groups_by_kernel_grid_and_run_order(tmp_path):
     assert ("attn_bf16_kernel<128, OutBf16>", "256", "") in rows
 
 
+def test_trace_reports_the_last_calls_of_a_run(tmp_path):
+    # a benchmark's warm-up calls come first: --last reports the timed calls on their own row
+    k = "void ra::(anonymous namespace)::attn_bf16_kernel<128, OutBf16>(ra::AttnArgs)"
+    spec = [(k, 1024, 9_000_000), (k, 1024, 3_000_000), (k, 1024, 5_000_000)]
+    write_csv(tmp_path / "kt.csv", TRACE_FIELDS, trace_rows(spec))
+    out = tmp_path / "t.md"
+    r = run_py("profile_summary.py", "trace", str(tmp_path / "kt.csv"), "--out", str(out), "--title", "T",
+               "--cmd", "C", "--split", "attn_bf16_kernel<128, OutBf16>@1024=bench",
+               "--last", "attn_bf16_kernel<128, OutBf16>@1024=bench:2")
+    assert r.returncode == 0, r.stderr
+    rows = {tuple(c.strip() for c in line.split("|")[1:4]): line.split("|") for line in out.read_text().splitlines()
+            if line.startswith("| attn")}
+    allr = rows[("attn_bf16_kernel<128, OutBf16>", "1024", "bench")]
+    last = rows[("attn_bf16_kernel<128, OutBf16>", "1024", "bench, last 2 calls")]
+    assert allr[4].strip() == "3" and float(allr[5]) == pytest.approx(17.0 / 3, abs=1e-3)
+    assert last[4].strip() == "2" and float(last[5]) == pytest.approx(4.0)   # (3 + 5) / 2 ms
+    assert float(last[6]) == pytest.approx(3.0) and float(last[7]) == pytest.approx(5.0)
+
+
 def pmc_rows(spec, counter):
     """spec: list of (kernel, grid, value); one row per dispatch for ``counter``."""
     return [{"Dispatch_Id": i, "Agent_Id": "Agent 1", "Kernel_Name": k, "Grid_Size": g, "Counter_Name": counter,
