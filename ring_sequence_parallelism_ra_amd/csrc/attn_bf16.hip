@@ -94,6 +94,9 @@ constexpr float kLn2 = 0.6931471805599453f;
 #ifndef RA_ATTN_SCHED_FIRST
 #define RA_ATTN_SCHED_FIRST 44        // VALU ops placed before the first MFMA of the main block
 #endif
+#ifndef RA_ATTN_KVS_GROUP_SYNC
+#define RA_ATTN_KVS_GROUP_SYNC 1      // key split: each wave group synchronises only its own waves per tile
+#endif
 #ifndef RA_ATTN_SOFFSET
 #define RA_ATTN_SOFFSET 1             // the copies' wave-uniform row offset as the scalar offset
 #endif
@@ -217,6 +220,9 @@ __global__ __launch_bounds__(NT * KVS, QB == 1 ? RA_ATTN_WAVES_PER_SIMD : 1) voi
   __shared__ __attribute__((aligned(1024))) __bf16 k_lds1[C::ELEMS * KVS];
   __shared__ __attribute__((aligned(1024))) __bf16 v_lds0[C::ELEMS * KVS];
   __shared__ __attribute__((aligned(1024))) __bf16 v_lds1[C::ELEMS * KVS];
+  // Key split: arrival counters of the two wave groups' own barrier (each group stages its tiles
+  // in its own LDS regions, so within the tile loop a group only waits for its own waves).
+  __shared__ uint32_t grp_sync[2];
 
   // tiles of one step visited before the next step
   constexpr int TG = PAIR == 2 ? TG_SHORT : (PAIR ? TG_PAIR : TG_ONE);
@@ -228,6 +234,7 @@ __global__ __launch_bounds__(NT * KVS, QB == 1 ? RA_ATTN_WAVES_PER_SIMD : 1) voi
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int hh = lane >> 5;
+  if (KVS == 2 && tid < 2) grp_sync[tid] = 0;  // visible to all waves after the prologue's barriers
 
   const int nbh = a.B * a.H;
   const int n_qt = (a.Sq + BM - 1) / BM;
